@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE-layer tokens/s of one MI355X's share of the fused MoE layer.
+
+One step = one ``moe_forward`` (route, EPLB remap, quant + dispatch, GEMM1 +
+SwiGLU + requant, GEMM2, combine) over the decode-share workload: 512 tokens,
+d_model 7168, d_ff 2048, 384 experts, top-6 sigmoid routing, 48 local experts
+(one EP8 rank's share), fp8 activations on MXFP4 experts, seeded synthetic
+inputs.  Inputs are resident in HBM before the timed region; the expert
+weights rotate over several device copies so that no step finds them in the
+256 MB MALL or in L2.
+
+Prints ONE JSON line (rank 0).  ``--gpus`` above 1 is refused: this build runs
+on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCES = ("moe_expert_layer_sigmoid_amd/csrc/kernels_gemm.hip",
+                "moe_expert_layer_sigmoid_amd/csrc/moe_device.hpp")
+
+
+def _src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm1_bytes(d, touched: int, rows: int) -> int:
+    """Algorithmic bytes of one GEMM1 launch: MXFP4 W1 + scales of every touched
+    slot, the fp8 rows and scales read, the requantised rows and scales written."""
+    w = touched * (2 * d.F * d.H // 2 + 2 * d.F * d.H // 32)
+    return w + rows * (d.H + d.H // 128) + rows * (d.F + d.F // 128)
+
+
+def layer_bytes(d, touched: int) -> int:
+    """Algorithmic bytes of the layer: all weights of touched slots, and per token
+    its logits (f32), input row and output row (bf16)."""
+    w = touched * (2 * d.F * d.H // 2 + 2 * d.F * d.H // 32 + d.H * d.F // 2 + d.H * d.F // 32)
+    return w + d.T * (d.E * 4 + d.H * 2 + d.H * 2)
+
+
+def run_gpu(cfg: int, steps: int, warmup: int, copies: int):
+    import torch
+    import moe_expert_layer_sigmoid_amd as mx
+    import synth
+
+    t0 = time.time()
+    wl = synth.make(cfg)
+    _log(f"[bench] inputs for cfg{cfg} generated in {time.time() - t0:.1f}s")
+    d = mx.Dims.of(wl.dims)
+    dev = "cuda"
+    x = torch.from_numpy(wl.x.view("int16")).to(dev)
+    logits = torch.from_numpy(wl.logits).to(dev)
+    rc = torch.from_numpy(wl.rep_count).to(dev)
+    rs = torch.from_numpy(wl.rep_slots).to(dev)
+    w = [tuple(torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s))]
+    for _ in range(copies - 1):
+        w.append(tuple(t.clone() for t in w[0]))
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
+    ws = mx.workspace(d)
+    taps = mx.make_taps(d)
+    chosen = mx.moe_forward(d, x, logits, *w[0], rc, rs, out, ws, taps=taps)
+    torch.cuda.synchronize()
+    counts = taps["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    rows = int(counts.sum())
+
+    def step(i):
+        mx.moe_forward(d, x, logits, *w[i % copies], rc, rs, out, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tw0 = time.perf_counter()
+    ev0.record(st)
+    for i in range(steps):
+        step(i)
+    ev1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw0
+    gpu_ms = ev0.elapsed_time(ev1)
+
+    # dominant kernel (GEMM1) alone, on the stream it is launched on
+    xq, xs, offs, aq, as_ = taps["xq"], taps["xs"], taps["offsets"], taps["aq"], taps["as_"]
+    for i in range(3):
+        mx.moe_grouped_gemm1_swiglu(d, xq, xs, offs, w[i % copies][0], w[i % copies][1], aq, as_, ws, stream=st)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(st)
+    for i in range(steps):
+        mx.moe_grouped_gemm1_swiglu(d, xq, xs, offs, w[i % copies][0], w[i % copies][1], aq, as_, ws, stream=st)
+    g1.record(st)
+    torch.cuda.synchronize()
+    g1_us = g0.elapsed_time(g1) * 1000.0 / steps
+    return dict(d=d, wl=wl, chosen=chosen, touched=touched, rows=rows, wall=wall, gpu_ms=gpu_ms,
+                gemm1_us=g1_us)
+
+
+def cpu_baseline(wl, n_slots: int):
+    """The oracle (float64 NumPy) on a bounded sample: the whole front end for
+    all tokens plus the expert work of the first ``n_slots`` local slots,
+    scaled to the full layer by P_local / n_slots."""
+    from oracle import moe as om
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    t0 = time.perf_counter()
+    om.forward(wl, slots=range(n_slots))
+    dt = time.perf_counter() - t0
+    d = wl.dims
+    est = dt * d.P_local / n_slots
+    return {"value": round(d.T / est, 3), "unit": "tokens/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": f"oracle forward of {d.T} tokens with expert work on {n_slots} of {d.P_local} "
+                      f"local slots ({dt:.1f}s), scaled x{d.P_local / n_slots:g}"}
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, valid
+    only while the GEMM sources are unchanged since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(f"{kernel}@{workload}")
+    if not e or e.get("src_hash") != _src_hash(GEMM_SOURCES):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3, help="weight copies rotated over steps")
+    ap.add_argument("--cfg", type=int, default=1, help=argparse.SUPPRESS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-slots", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported"}))
+        sys.exit(2)
+
+    r = run_gpu(args.cfg, args.steps, args.warmup, args.copies)
+    d = r["d"]
+    ms = r["wall"] * 1000.0 / args.steps
+    value = d.T * args.steps / r["wall"]
+    g1_bytes = gemm1_bytes(d, r["touched"], r["rows"])
+    g1_gbs = g1_bytes / (r["gemm1_us"] * 1e-6) / 1e9
+    lay_bytes = layer_bytes(d, r["touched"])
+    lay_gbs = lay_bytes / (ms * 1e-3) / 1e9
+    flops = 2 * r["rows"] * (2 * d.F * d.H + d.H * d.F)
+    line = {
+        "metric": "MoE-layer tokens/s per GPU (512 & 8192 tok/rank); % HBM BW / MFMA peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x mxfp4 (f32 accumulate)",
+        "data": "synthetic (seeded; random-init MXFP4 experts)",
+        "config": {"workload": "decode share: T=512 tokens, d_model 7168, d_ff 2048, 384 experts, top-6 "
+                               "sigmoid, 48 local experts, a8w4",
+                   "T": d.T, "H": d.H, "F": d.F, "E": d.E, "k": d.k, "P_local": d.P_local,
+                   "path": r["chosen"], "touched_slots": r["touched"], "rows": r["rows"],
+                   "weight_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "k_gemm1_stream", "achieved": round(g1_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile("k_gemm1_stream", "cfg1"),
+                     "bytes_per_launch": g1_bytes, "avg_launch_us": round(r["gemm1_us"], 2)},
+        "layer_roofline": {"bound": "hbm", "achieved": round(lay_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(lay_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": lay_bytes,
+                           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 5),
+                           "gpu_event_ms_per_step": round(r["gpu_ms"] / args.steps, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(r["wl"], args.cpu_slots)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * moe.h -- C ABI of libmoe: one MI355X's share of a fused Mixture-of-Experts
+ * layer (sigmoid top-k routing, EPLB remap + load recording, fp8 activations
+ * on MXFP4 experts), as hand-written HIP kernels for gfx950.
+ *
+ * What the layer is, from the pages:
+ *  - The MegaMoEV2 operator runs quant, dispatch, GEMM1, GEMM2 and combine;
+ *    its small-input path does all of them in one kernel for up to 512 tokens
+ *    per rank, and its persistent large-input path serves extend steps of at
+ *    least 1024 tokens [sglang PR 47065 "[Perf] [AMD] dsv4: Use the aiter
+ *    MegaMoE small- and large-input paths", intro and Modifications].
+ *  - Activations are fp8 and routed experts MXFP4 ("a8w4") [InferenceX PR 3430
+ *    "[AMD][MI35X] 0926 DSV4 sglang mtp agentic", Additional detail section].
+ *  - Each token picks its top-6 routed experts [sglang PR 35619 "Aiter/FlyDSL
+ *    MegaMoEv2 backend for DeepSeek-V4", "Four settings that silently break
+ *    it", item 2].
+ *  - Prefill fuses the EPLB logical-to-physical remap with load recording
+ *    [same page, Summary]; EPLB runs with redundant physical experts
+ *    [FlyDSL issue 978 "Investigate MegaMoEV2 end-to-end throughput gap vs V1
+ *    on 8xMI355X", Benchmark plan].
+ *  The pages print no formula; the readings used for the unstated steps are:
+ *  sigmoid scores and renormalised top-k weights, replica = MurmurHash3
+ *  fmix32(global token id) mod replica count, e8m0 per-128-column activation
+ *  scales, SwiGLU between the GEMMs, routing weights applied in the combine.
+ *
+ * Conventions for every call
+ *  - Pointers other than `dims`, `taps` and `chosen` are DEVICE pointers owned
+ *    by the caller; they must be 16-byte aligned.  The library allocates
+ *    nothing and keeps no state between calls.
+ *  - Every call is asynchronous on `stream` (NULL = the default stream); it
+ *    never synchronises the host and never prints.
+ *  - Arguments are validated on the host before any launch; a failed check
+ *    returns a negative moe_status_t and launches nothing.  A launch error
+ *    becomes MOE_ERR_HIP.  Finite inputs, expert ids in [0, E) and replica
+ *    tables whose entries lie in [0, P_total) are the caller's contract.
+ *  - T == 0 is valid and launches nothing (the outputs have no rows).
+ *  - Calls on one workspace must not overlap in time; use one workspace per
+ *    stream for concurrent calls.
+ *
+ * Layouts (row-major, C order):
+ *  logits   f32  [T, E]
+ *  x        bf16 [T, H]                 (uint16 bit patterns)
+ *  w1       u8   [P_local, 2F, H/2]     e2m1 pairs, element 2i in the low nibble;
+ *                                       rows [0, F) gate, [F, 2F) up
+ *  w1s      u8   [P_local, 2F, H/32]    e8m0 scale of each 32-element block along K
+ *  w2       u8   [P_local, H, F/2]
+ *  w2s      u8   [P_local, H, F/32]
+ *  rep_count  i32 [E]                   replicas of each logical expert (>= 1)
+ *  rep_slots  i32 [E, R_max]            physical slot of replica r of expert e
+ *  load_hist  i32 [P_total]             += pairs per physical slot (nullable)
+ *  topk_ids i32 [T, k], topk_w f32 [T, k], phys_ids i32 [T, k]
+ *  counts   i32 [P_local], offsets i32 [P_local + 1]
+ *  row_of_pair i32 [T*k] (-1: remote pair), pair_of_row i32 [T_max*k]
+ *  xq u8 [T_max*k, H] (fp8 e4m3fn), xs u8 [T_max*k, H/128] (e8m0)
+ *  aq u8 [T_max*k, F], as u8 [T_max*k, F/128]
+ *  out bf16 [T, H]
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad shape or misaligned pointer */
+  MOE_ERR_UNSUPPORTED = -2, /* a size beyond the limits below */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = -4          /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum {
+  MOE_PATH_AUTO = 0,    /* SMALL_M if T <= small_m_max, LARGE_M if T >= large_m_min, else STAGED */
+  MOE_PATH_SMALL_M = 1, /* weight-streaming kernels for a few rows per expert */
+  MOE_PATH_STAGED = 2,  /* the component calls in sequence */
+  MOE_PATH_LARGE_M = 3  /* tiled kernels for many rows per expert */
+} moe_path_t;
+
+/* Problem sizes of one call.  Limits: 0 <= T <= T_max <= 1<<20; H, F
+ * multiples of 128, each in [128, 16384]; 1 <= E <= 1024; 1 <= k <= min(E, 16);
+ * 1 <= P_total <= 1024; 0 <= p0, 1 <= P_local, p0 + P_local <= P_total;
+ * 1 <= R_max <= 64.  Without EPLB: P_total = E, R_max = 1, rep_slots[e] = e. */
+typedef struct {
+  int32_t T, T_max;
+  int32_t H, F, E, k;
+  int32_t P_total, p0, P_local, R_max;
+  uint32_t token_id_base;  /* global id of token 0; the remap hashes global ids */
+  int32_t small_m_max;     /* 0 -> 512  [sglang PR 47065, intro]            */
+  int32_t large_m_min;     /* 0 -> 1024 [sglang PR 47065, Modifications]    */
+} moe_dims_t;
+
+/* Optional device copies of intermediate results for parity checks; any
+ * member may be NULL.  Shapes as in the layout table above. */
+typedef struct {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* phys_ids;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_of_pair;
+  int32_t* pair_of_row;
+  uint8_t* xq;
+  uint8_t* xs;
+  uint8_t* aq;
+  uint8_t* as;
+} moe_taps_t;
+
+/* Bytes of device workspace every call below needs for `dims` (sized by
+ * T_max, independent of T).  Returns 0 for invalid dims. */
+size_t moe_workspace_bytes(const moe_dims_t* dims);
+
+/* The path MOE_PATH_AUTO takes for `dims`: small-input at most small_m_max
+ * tokens, large-input from large_m_min tokens, staged in between
+ * [sglang PR 47065, intro and Modifications; the aiter commit note on the
+ * three-state large-input switch]. */
+moe_path_t moe_select_path(const moe_dims_t* dims);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* a1. Top-k routing [sglang PR 35619, "Four settings that silently break it"].
+ * For each token: the k largest logits (descending, equal logits to the lower
+ * expert id); weight_j = sigmoid(l_j) / sum_i sigmoid(l_i) in f32. */
+int moe_route(const moe_dims_t* dims, const float* logits, int32_t* topk_ids, float* topk_w,
+              moe_stream_t stream);
+
+/* a2. EPLB logical -> physical remap with load recording [sglang PR 35619,
+ * Summary; FlyDSL issue 978, Data-quality gates].
+ * phys[t][j] = rep_slots[e][fmix32(token_id_base + t) mod rep_count[e]],
+ * e = topk_ids[t][j]; if load_hist != NULL, load_hist[p] += number of pairs
+ * with phys == p (all T*k pairs, every slot).  Deterministic, no atomics. */
+int moe_eplb_remap_record(const moe_dims_t* dims, const int32_t* topk_ids, const int32_t* rep_count,
+                          const int32_t* rep_slots, int32_t* phys_ids, int32_t* load_hist,
+                          void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* a3 + a4. Bucket this GPU's pairs by local slot and quantise + dispatch the
+ * activations [sglang PR 47065, intro: "quant, dispatch"].
+ * Local pairs have p0 <= phys < p0 + P_local; slot s = phys - p0 owns rows
+ * [offsets[s], offsets[s+1]), filled in ascending (t, j).  Row r holds token
+ * pair_of_row[r] / k quantised per 128 columns: scale byte e + 127 with e the
+ * smallest integer such that amax <= 448 * 2^e, codes RNE_e4m3fn(x * 2^-e). */
+int moe_quant_permute(const moe_dims_t* dims, const uint16_t* x, const int32_t* phys_ids,
+                      uint8_t* xq, uint8_t* xs, int32_t* counts, int32_t* offsets,
+                      int32_t* row_of_pair, int32_t* pair_of_row,
+                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* a5. GEMM1 + SwiGLU + fp8 requant, grouped by slot [sglang PR 47065, intro].
+ * For each row r of slot s: h = W1_s a_r (f32 accumulation of block-scaled
+ * fp8 x MXFP4 products); act_f = silu(h_f) * h_{F+f}; act requantised with
+ * the a4 rule per 128 columns into aq / as.  `offsets` as from a3. */
+int moe_grouped_gemm1_swiglu(const moe_dims_t* dims, const uint8_t* xq, const uint8_t* xs,
+                             const int32_t* offsets, const uint8_t* w1, const uint8_t* w1s,
+                             uint8_t* aq, uint8_t* as, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream);
+
+/* a6 + a7. GEMM2 and the routing-weighted combine [sglang PR 47065, intro].
+ * y_r = W2_s dequant(aq_r) (f32); out[t] = bf16_rne(sum over local j, ascending,
+ * of topk_w[t][j] * y[row_of_pair[t*k+j]]); tokens with no local pair get +0. */
+int moe_grouped_gemm2_combine(const moe_dims_t* dims, const uint8_t* aq, const uint8_t* as,
+                              const int32_t* offsets, const uint8_t* w2, const uint8_t* w2s,
+                              const int32_t* row_of_pair, const float* topk_w, uint16_t* out,
+                              void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* The whole layer, a1..a7, on `path` (MOE_PATH_AUTO: moe_select_path).
+ * rep_count / rep_slots describe the replica table; load_hist (nullable) is
+ * accumulated as in a2 (pass NULL in decode: recording is prefill-only
+ * [sglang PR 35619, Summary]).  `chosen` (host, nullable) receives the path
+ * taken.  `taps` (host struct of device pointers, nullable) receives copies
+ * of the intermediates. */
+int moe_forward(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, const float* logits,
+                const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2, const uint8_t* w2s,
+                const int32_t* rep_count, const int32_t* rep_slots, int32_t* load_hist,
+                uint16_t* out, const moe_taps_t* taps, moe_path_t* chosen,
+                void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,261 @@
+// C ABI of libmoe: host-side validation, workspace layout and the launch
+// sequences of the fused MoE layer (see include/moe.h for the contract).
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  size_t ids, w, phys, rank, partial, base, counts, offsets, rop, por, xq, xs, aq, as, y, total;
+};
+
+// One workspace serves every call; regions are sized by T_max.
+Layout layout_of(const moe_dims_t* d) {
+  Layout L{};
+  const size_t TK = (size_t)d->T_max * d->k;
+  const size_t nch = ((size_t)d->T_max + kChunkTokens - 1) / kChunkTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += round_up(bytes, kAlign);
+    return o;
+  };
+  L.ids = take(TK * 4);
+  L.w = take(TK * 4);
+  L.phys = take(TK * 4);
+  L.rank = take(TK * 4);
+  L.partial = take(nch * d->P_total * 4);
+  L.base = take(nch * d->P_local * 4);
+  L.counts = take((size_t)d->P_local * 4);
+  L.offsets = take(((size_t)d->P_local + 1) * 4);
+  L.rop = take(TK * 4);
+  L.por = take(TK * 4);
+  L.xq = take(TK * d->H);
+  L.xs = take(TK * (d->H / kActBlock));
+  L.aq = take(TK * d->F);
+  L.as = take(TK * (d->F / kActBlock));
+  L.y = take(TK * d->H * 4);
+  L.total = off;
+  return L;
+}
+
+int check_dims(const moe_dims_t* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->T_max < 0 || d->T > d->T_max) return MOE_ERR_INVALID_ARG;
+  if (d->T_max > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  if (d->H <= 0 || d->F <= 0 || d->H % 128 || d->F % 128) return MOE_ERR_INVALID_ARG;
+  if (d->H > 16384 || d->F > 16384) return MOE_ERR_UNSUPPORTED;
+  if (d->E < 1 || d->k < 1 || d->k > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->E > 1024 || d->k > 16) return MOE_ERR_UNSUPPORTED;
+  if (d->P_total < 1 || d->P_local < 1 || d->p0 < 0 || d->p0 + d->P_local > d->P_total) return MOE_ERR_INVALID_ARG;
+  if (d->P_total > 1024) return MOE_ERR_UNSUPPORTED;
+  if (d->R_max < 1) return MOE_ERR_INVALID_ARG;
+  if (d->R_max > 64) return MOE_ERR_UNSUPPORTED;
+  if (d->small_m_max < 0 || d->large_m_min < 0) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool dev_ok(const void* p) { return p != nullptr && aligned(p); }
+bool opt_ok(const void* p) { return p == nullptr || aligned(p); }
+
+int check_ws(const moe_dims_t* d, void* ws, size_t bytes) {
+  size_t need = layout_of(d).total;
+  if (need == 0) return MOE_OK;
+  if (!ws || bytes < need) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws % kAlign) != 0) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+int nchunks(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_dims_t* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return layout_of(dims).total;
+}
+
+moe_path_t moe_select_path(const moe_dims_t* d) {
+  if (!d) return MOE_PATH_AUTO;
+  const int small = d->small_m_max > 0 ? d->small_m_max : 512;
+  const int large = d->large_m_min > 0 ? d->large_m_min : 1024;
+  if (d->T <= small) return MOE_PATH_SMALL_M;
+  if (d->T >= large) return MOE_PATH_LARGE_M;
+  return MOE_PATH_STAGED;
+}
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_ids, float* topk_w, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(logits) || !dev_ok(topk_ids) || !dev_ok(topk_w)) return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
+  return hip_status(launch_route(logits, d->T, d->E, d->k, topk_ids, topk_w, (hipStream_t)stream));
+}
+
+int moe_eplb_remap_record(const moe_dims_t* d, const int32_t* topk_ids, const int32_t* rep_count,
+                          const int32_t* rep_slots, int32_t* phys_ids, int32_t* load_hist, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(topk_ids) || !dev_ok(rep_count) || !dev_ok(rep_slots) || !dev_ok(phys_ids) || !opt_ok(load_hist))
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(d, ws, ws_bytes))) return rc;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Layout L = layout_of(d);
+  int32_t* partial = load_hist ? at<int32_t>(ws, L.partial) : nullptr;
+  MOE_TRY(launch_count(d->T, d->k, topk_ids, rep_count, rep_slots, d->R_max, d->token_id_base, phys_ids, true,
+                       d->P_total, d->p0, d->P_local, partial, nullptr, st));
+  if (load_hist)
+    MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, nullptr, nullptr, nullptr, load_hist,
+                        st));
+  return MOE_OK;
+}
+
+int moe_quant_permute(const moe_dims_t* d, const uint16_t* x, const int32_t* phys_ids, uint8_t* xq, uint8_t* xs,
+                      int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row, void* ws,
+                      size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(x) || !dev_ok(phys_ids) || !dev_ok(xq) || !dev_ok(xs) || !dev_ok(counts) || !dev_ok(offsets) ||
+      !dev_ok(row_of_pair) || !dev_ok(pair_of_row))
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(d, ws, ws_bytes))) return rc;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Layout L = layout_of(d);
+  int32_t* partial = at<int32_t>(ws, L.partial);
+  int32_t* rank = at<int32_t>(ws, L.rank);
+  int32_t* base = at<int32_t>(ws, L.base);
+  MOE_TRY(launch_count(d->T, d->k, nullptr, nullptr, nullptr, d->R_max, d->token_id_base,
+                       const_cast<int32_t*>(phys_ids), false, d->P_total, d->p0, d->P_local, partial, rank, st));
+  MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, counts, offsets, base, nullptr, st));
+  MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys_ids, d->p0, d->P_local, base, rank, xq, xs, row_of_pair,
+                       pair_of_row, st));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm1_swiglu(const moe_dims_t* d, const uint8_t* xq, const uint8_t* xs, const int32_t* offsets,
+                             const uint8_t* w1, const uint8_t* w1s, uint8_t* aq, uint8_t* as, void* ws,
+                             size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(xq) || !dev_ok(xs) || !dev_ok(offsets) || !dev_ok(w1) || !dev_ok(w1s) || !dev_ok(aq) || !dev_ok(as))
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(d, ws, ws_bytes))) return rc;
+  if (d->T == 0) return MOE_OK;
+  return hip_status(launch_gemm1_stream(xq, xs, offsets, w1, w1s, aq, as, d->H, d->F, d->P_local,
+                                        (hipStream_t)stream));
+}
+
+int moe_grouped_gemm2_combine(const moe_dims_t* d, const uint8_t* aq, const uint8_t* as, const int32_t* offsets,
+                              const uint8_t* w2, const uint8_t* w2s, const int32_t* row_of_pair, const float* topk_w,
+                              uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(aq) || !dev_ok(as) || !dev_ok(offsets) || !dev_ok(w2) || !dev_ok(w2s) || !dev_ok(row_of_pair) ||
+      !dev_ok(topk_w) || !dev_ok(out))
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(d, ws, ws_bytes))) return rc;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Layout L = layout_of(d);
+  float* y = at<float>(ws, L.y);
+  MOE_TRY(launch_gemm2_stream(aq, as, offsets, w2, w2s, y, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_combine(d->T, d->H, d->k, y, row_of_pair, topk_w, out, st));
+  return MOE_OK;
+}
+
+int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const float* logits, const uint8_t* w1,
+                const uint8_t* w1s, const uint8_t* w2, const uint8_t* w2s, const int32_t* rep_count,
+                const int32_t* rep_slots, int32_t* load_hist, uint16_t* out, const moe_taps_t* taps,
+                moe_path_t* chosen, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
+  if (!dev_ok(x) || !dev_ok(logits) || !dev_ok(w1) || !dev_ok(w1s) || !dev_ok(w2) || !dev_ok(w2s) ||
+      !dev_ok(rep_count) || !dev_ok(rep_slots) || !opt_ok(load_hist) || !dev_ok(out))
+    return MOE_ERR_INVALID_ARG;
+  if (taps) {
+    const void* tp[] = {taps->topk_ids, taps->topk_w, taps->phys_ids, taps->counts, taps->offsets, taps->row_of_pair,
+                        taps->pair_of_row, taps->xq, taps->xs, taps->aq, taps->as};
+    for (const void* p : tp)
+      if (!opt_ok(p)) return MOE_ERR_INVALID_ARG;
+  }
+  if ((rc = check_ws(d, ws, ws_bytes))) return rc;
+  const moe_path_t p = path == MOE_PATH_AUTO ? moe_select_path(d) : path;
+  if (chosen) *chosen = p;
+  if (d->T == 0) return MOE_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  Layout L = layout_of(d);
+  auto pick = [&](auto* tap, size_t off) -> decltype(tap) {
+    return tap ? tap : reinterpret_cast<decltype(tap)>(static_cast<char*>(ws) + off);
+  };
+  const moe_taps_t none{};
+  const moe_taps_t& tp = taps ? *taps : none;
+  int32_t* ids = pick(tp.topk_ids, L.ids);
+  float* w = pick(tp.topk_w, L.w);
+  int32_t* phys = pick(tp.phys_ids, L.phys);
+  int32_t* counts = pick(tp.counts, L.counts);
+  int32_t* offsets = pick(tp.offsets, L.offsets);
+  int32_t* rop = pick(tp.row_of_pair, L.rop);
+  int32_t* por = pick(tp.pair_of_row, L.por);
+  uint8_t* xq = pick(tp.xq, L.xq);
+  uint8_t* xs = pick(tp.xs, L.xs);
+  uint8_t* aq = pick(tp.aq, L.aq);
+  uint8_t* as = pick(tp.as, L.as);
+  int32_t* rank = at<int32_t>(ws, L.rank);
+  int32_t* partial = at<int32_t>(ws, L.partial);
+  int32_t* base = at<int32_t>(ws, L.base);
+  float* y = at<float>(ws, L.y);
+
+  MOE_TRY(launch_route(logits, d->T, d->E, d->k, ids, w, st));
+  MOE_TRY(launch_count(d->T, d->k, ids, rep_count, rep_slots, d->R_max, d->token_id_base, phys, true, d->P_total,
+                       d->p0, d->P_local, partial, rank, st));
+  MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, counts, offsets, base, load_hist, st));
+  MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys, d->p0, d->P_local, base, rank, xq, xs, rop, por, st));
+  MOE_TRY(launch_gemm1_stream(xq, xs, offsets, w1, w1s, aq, as, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_gemm2_stream(aq, as, offsets, w2, w2s, y, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, st));
+  return MOE_OK;
+}
+
+}  // extern "C"

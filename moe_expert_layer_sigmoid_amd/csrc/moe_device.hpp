@@ -1,0 +1,83 @@
+// Device helpers shared by the gfx950 kernels of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kActBlock = 128;   // activation scale block (columns)
+constexpr int kChunkTokens = 64; // tokens per counting chunk
+
+// MFMA operand format codes of the block-scaled f8f6f4 instructions.
+constexpr int kFmtFp8 = 0;  // e4m3fn
+constexpr int kFmtFp4 = 4;  // e2m1
+
+// MurmurHash3's 32-bit finaliser (Appleby, public domain): the replica hash
+// of the EPLB remap.
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// Smallest integer e with amax <= 448 * 2^e (0 when amax == 0), clamped to
+// [-127, 127].  With amax = f * 2^x, f in [0.5, 1) and 448 = 0.875 * 2^9:
+// e = x - 9 when f <= 0.875, else x - 8.  Exact for every finite amax.
+__device__ __forceinline__ int scale_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int x;
+  float f = frexpf(amax, &x);
+  int e = x - 9 + (f > 0.875f ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four f32 values (each |v| <= 448) -> four e4m3fn codes, round to nearest
+// even, packed little-endian (v0 in the low byte).
+__device__ __forceinline__ uint32_t pack4_fp8(float v0, float v1, float v2, float v3) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, p, true);
+  return (uint32_t)p;
+}
+
+// f32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  uint32_t b = __float_as_uint(v);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Block index -> work item such that consecutive items land on the same XCD.
+// The hardware deals workgroups round-robin over the 8 XCDs (block b runs on
+// XCD b % 8); items of one expert share activation rows, so keeping them on
+// one XCD keeps those rows in that XCD's L2.
+__device__ __forceinline__ int xcd_item(int b, int nblk) {
+  const int nx = 8;
+  int xcd = b % nx, idx = b / nx;
+  int q = nblk / nx, rem = nblk % nx;
+  return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+}
+
+// Block-scaled 16x16x128 MFMA, A = MXFP4 (e2m1, 32 K-elements in the 4 low
+// dwords of each lane), B = fp8 e4m3fn, f32 accumulate.  Lane l supplies
+// row/column l % 16 and scale block l / 16; `OPSEL_A` picks the byte of
+// `sa` that holds this lane's A scale, B's scale is the low byte of `sb`.
+template <int OPSEL_A>
+__device__ __forceinline__ v4f mfma_fp4_fp8(v4i a, v8i b, v4f c, int sa, int sb) {
+  v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, kFmtFp4, kFmtFp8, OPSEL_A, sa, 0, sb);
+}
+
+}  // namespace moe

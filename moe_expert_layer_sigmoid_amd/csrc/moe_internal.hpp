@@ -1,0 +1,41 @@
+// Host-side launch wrappers of the libmoe kernels (internal; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Front kernels (kernels_front.hip)
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
+
+// Remap (optional), per-chunk histogram partials and local ranks.
+//  do_remap: phys = rep_slots[e][fmix32(base + t) % rep_count[e]] from ids; else phys is input.
+//  partial:  [nch, P_total] counts per chunk of 64 tokens (nullable)
+//  rank:     [T*k] rank of each local pair among the chunk's pairs of its slot (nullable)
+hipError_t launch_count(int T, int k, const int32_t* ids, const int32_t* rep_count, const int32_t* rep_slots,
+                        int R_max, uint32_t token_id_base, int32_t* phys, bool do_remap, int P_total, int p0,
+                        int P_local, int32_t* partial, int32_t* rank, hipStream_t st);
+
+// Sum chunk partials: counts/offsets/base of local slots (when counts != NULL)
+// and load_hist += totals over all slots (when load_hist != NULL).
+hipError_t launch_scan(int nch, int P_total, int p0, int P_local, const int32_t* partial, int32_t* counts,
+                       int32_t* offsets, int32_t* base, int32_t* load_hist, hipStream_t st);
+
+// Row assignment + fp8 quantisation + dispatch of each token to its local rows.
+hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* phys, int p0, int P_local,
+                        const int32_t* base, const int32_t* rank, uint8_t* xq, uint8_t* xs,
+                        int32_t* row_of_pair, int32_t* pair_of_row, hipStream_t st);
+
+hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* row_of_pair, const float* w,
+                          uint16_t* out, hipStream_t st);
+
+// GEMM kernels (kernels_gemm.hip)
+hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* w1,
+                               const uint8_t* w1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
+                               hipStream_t st);
+hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* w2,
+                               const uint8_t* w2s, float* y, int H, int F, int P_local, hipStream_t st);
+
+}  // namespace moe

@@ -333,12 +333,16 @@ def requant_tie_zone(act: np.ndarray, eps: np.ndarray, block: int = BLOCK_ACT):
 
 
 def act_error_bound(a: np.ndarray, w1: np.ndarray, w1s: np.ndarray, h: np.ndarray, F: int,
-                    rel: float = 2.0 ** -18) -> np.ndarray:
-    """A generous bound on |act_f32 - act| for the tie-zone test.
+                    rel: float = 2.0 ** -14) -> np.ndarray:
+    """A bound on |act_gpu - act| for the requant tie-zone test.
 
-    The f32 accumulation error of h is taken as ``rel`` * sum_k |a_k w_k|
-    (about 64 roundings of unit 2^-24 over a sum of absolute terms), and
-    propagated through silu(g) * u to first order, plus a few f32 ulps of act.
+    The GPU accumulates h with block-scaled fp8 x fp4 MFMA instructions that
+    round inside the instruction: measured on gfx950, a single K = 128
+    instruction is off by up to 2.5e-5 * sum_k |a_k w_k| and longer sums stay
+    within the same ratio (each instruction's error is bounded by its own
+    share of the absolute sum).  The bound takes ``rel`` = 2^-14 (2.4x the
+    largest observation) times sum_k |a_k w_k|, propagates it through
+    silu(g) * u to first order, and adds a few f32 ulps of act.
     """
     W = np.abs(fm.dequant_mxfp4(w1, w1s))
     mag = np.abs(a) @ W.T
@@ -347,4 +351,5 @@ def act_error_bound(a: np.ndarray, w1: np.ndarray, w1s: np.ndarray, h: np.ndarra
     sg = sigmoid(g)
     dsilu = sg * (1.0 + g * (1.0 - sg))
     act = g * sg * u
-    return np.abs(dsilu * u) * eh[:, :F] + np.abs(g * sg) * eh[:, F:] + 2.0 ** -21 * np.abs(act)
+    return (np.abs(dsilu * u) * eh[:, :F] + np.abs(g * sg) * eh[:, F:] + eh[:, :F] * eh[:, F:]
+            + 2.0 ** -21 * np.abs(act))

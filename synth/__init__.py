@@ -15,5 +15,6 @@ from .inputs import (  # noqa: F401
     make,
     make_ep_shaped,
     make_sweep,
+    make_custom,
     sha256,
 )

@@ -400,3 +400,34 @@ def make_ep_shaped(ranks: int = 8, T_rank: int = 8192, with_weights: bool = True
     return Workload(name=f"cfg2_ep{ranks}", dims=d, logits=logits, x=x,
                     rep_count=base.rep_count, rep_slots=base.rep_slots,
                     slot_expert=base.slot_expert, w1=w.w1, w1s=w.w1s, w2=w.w2, w2s=w.w2s)
+
+
+def make_custom(T: int, H: int, F: int, E: int, k: int, P_local: int, p0: int = 0,
+                redundant: int = 0, ranks: int = 1, seed: int = 100, token_id_base: int = 0,
+                T_max: Optional[int] = None, zipf_s: Optional[float] = None) -> Workload:
+    """A workload of arbitrary shape (parity cases that span several tiles and
+    ragged tails).  ``redundant`` > 0 adds replicas by the greedy map over a
+    uniform (or Zipf, if ``zipf_s``) popularity; physical slots are spread over
+    ``ranks`` ranks and this GPU holds [p0, p0 + P_local)."""
+    pop = None
+    bias = None
+    if zipf_s is not None:
+        pop = zipf_popularity(E, k, zipf_s, _rng(seed, STREAM_EPLB, 0))
+        bias = zipf_bias(pop, k)
+    if redundant > 0:
+        p = pop if pop is not None else np.full(E, 1.0 / E)
+        rep_count, rep_slots, all_slot_expert = greedy_replica_map(p, redundant, ranks)
+    else:
+        rep_count, rep_slots = _identity_map(E)
+        all_slot_expert = np.arange(E, dtype=np.int32)
+    P_total = E + redundant
+    d = Dims(T=T, T_max=T if T_max is None else T_max, H=H, F=F, E=E, k=k, P_total=P_total, p0=p0,
+             P_local=P_local, R_max=rep_slots.shape[1], token_id_base=token_id_base)
+    if p0 < 0 or p0 + P_local > P_total:
+        raise ValueError("local slot window out of range")
+    slot_expert = all_slot_expert[p0:p0 + P_local].copy()
+    logits, x = _tokens(seed, 0, T, H, E, bias)
+    w1, w1s, w2, w2s = _slot_weights(1000 + seed, H, F, slot_expert)
+    return Workload(name=f"custom_T{T}_H{H}_F{F}_E{E}_k{k}", dims=d, logits=logits, x=x,
+                    rep_count=rep_count, rep_slots=rep_slots, slot_expert=slot_expert,
+                    w1=w1, w1s=w1s, w2=w2, w2s=w2s, popularity=pop)

@@ -1,0 +1,111 @@
+"""The C-ABI library loads on the CPU, exports every declared symbol, and
+rejects bad arguments on the host before any launch (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_expert_layer_sigmoid_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mx.LIB_PATH), reason="libmoe.so not built")
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names |= set(re.findall(r"\b(moe_\w+)\s*\(", txt))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    decl = _declared()
+    assert set(mx.EXPORTS) <= decl
+    L = mx.lib()
+    for n in sorted(decl):
+        assert hasattr(L, n), n
+
+
+def _dims(**kw):
+    base = dict(T=512, T_max=512, H=7168, F=2048, E=384, k=6, P_total=384, p0=0, P_local=48, R_max=1)
+    base.update(kw)
+    return mx.Dims(**base)
+
+
+def test_workspace_bytes_and_invalid_dims():
+    d = _dims()
+    n = mx.moe_workspace_bytes(d)
+    rows = 512 * 6
+    assert n >= rows * (7168 + 56 + 2048 + 16 + 7168 * 4)
+    assert mx.moe_workspace_bytes(_dims(T=8192, T_max=8192)) > n
+    for bad in (dict(T=513), dict(H=100), dict(F=0), dict(k=0), dict(k=17), dict(E=2000),
+                dict(P_local=0), dict(p0=340), dict(R_max=0), dict(P_total=2000), dict(T=-1)):
+        assert mx.moe_workspace_bytes(_dims(**bad)) == 0, bad
+    # depends on T_max only
+    assert mx.moe_workspace_bytes(_dims(T=1)) == n
+
+
+def test_select_path_thresholds():
+    assert mx.moe_select_path(_dims(T=1)) == "small_m"
+    assert mx.moe_select_path(_dims(T=512)) == "small_m"
+    assert mx.moe_select_path(_dims(T=513, T_max=8192)) == "staged"
+    assert mx.moe_select_path(_dims(T=1023, T_max=8192)) == "staged"
+    assert mx.moe_select_path(_dims(T=1024, T_max=8192)) == "large_m"
+    assert mx.moe_select_path(_dims(T=100, small_m_max=64, large_m_min=100)) == "large_m"
+    assert mx.moe_select_path(_dims(T=64, small_m_max=64)) == "small_m"
+
+
+def test_status_strings():
+    for c in (0, -1, -2, -3, -4, 7):
+        assert mx.moe_status_string(c)
+
+
+def _forward_raw(d, ptrs, ws, ws_bytes, path=0):
+    L = mx.lib()
+    chosen = ctypes.c_int(-1)
+    P = ctypes.c_void_p
+    rc = L.moe_forward(ctypes.byref(d), path, *[P(p) if p else None for p in ptrs], None,
+                       ctypes.byref(chosen), P(ws) if ws else None, ws_bytes, None)
+    return rc, chosen.value
+
+
+GOOD = [0x1000 * (i + 1) for i in range(10)]  # aligned fake device addresses, never dereferenced
+
+
+def test_host_validation_before_launch():
+    d = _dims()
+    need = mx.moe_workspace_bytes(d)
+    # null required pointer
+    p = list(GOOD)
+    p[0] = 0
+    assert _forward_raw(d, p, 0x100000, need)[0] == -1
+    # misaligned pointer
+    p = list(GOOD)
+    p[3] = 0x1008
+    assert _forward_raw(d, p, 0x100000, need)[0] == -1
+    # workspace missing / too small
+    assert _forward_raw(d, GOOD, 0, 0)[0] == -3
+    assert _forward_raw(d, GOOD, 0x100000, need - 1)[0] == -3
+    # T > T_max, k mismatch analog, unsupported sizes
+    assert _forward_raw(_dims(T=600), GOOD, 0x100000, need)[0] == -1
+    assert _forward_raw(_dims(k=17), GOOD, 0x100000, need)[0] == -2
+    assert _forward_raw(_dims(H=200), GOOD, 0x100000, need)[0] == -1
+    # bad path
+    assert _forward_raw(d, GOOD, 0x100000, need, path=9)[0] == -1
+
+
+def test_zero_tokens_is_a_no_op():
+    d = _dims(T=0)
+    need = mx.moe_workspace_bytes(d)
+    rc, chosen = _forward_raw(d, GOOD, 0x100000, need)
+    assert rc == 0 and chosen == 1  # small-M, nothing launched
+    L = mx.lib()
+    P = ctypes.c_void_p
+    assert L.moe_route(ctypes.byref(d), P(0x1000), P(0x2000), P(0x3000), None) == 0
+    assert L.moe_route(ctypes.byref(d), None, P(0x2000), P(0x3000), None) == -1

@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases are compared stage by stage in full; the full-size workloads
+(T = 512 / 8192 with the 7168 x 2048 experts) are compared in full on every
+integer stage and on the activation quantisation, and on sampled experts and
+tokens for the GEMM stages (the oracle computes those one expert at a time).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_layer_sigmoid_amd as mx
+import synth
+from oracle import formats as fm
+from oracle import moe as om
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _full_check(wl, path="auto"):
+    """Every stage in full against the oracle's whole forward."""
+    d = wl.dims
+    _say(f"[case] {wl.name} T={d.T} H={d.H} F={d.F} E={d.E} k={d.k} P={d.P_total}/{d.p0}+{d.P_local} path={path}")
+    res = P.run_forward(wl, path=path)
+    ref = P.oracle_front(wl)
+    P.check_front(res, ref, d)
+    y_c, (nd, ns) = P.expert_check(wl, res, ref, range(d.P_local))
+    full = om.forward(wl)
+    toks = list(range(d.T))
+    cond = P.conditioned_out(toks, ref, y_c, d)
+    n1 = P.check_out(res["out"], cond, "conditioned")
+    n2, _ = P.rel_errors(fm.bf16_to_f64(res["out"]), full["out"])
+    assert n2 <= P.OUT_NORM_TOL, f"unconditioned normwise {n2}"
+    # tokens without local pairs are exactly +0
+    none_local = (ref["row_of_pair"].reshape(d.T, d.k) < 0).all(1)
+    assert np.all(res["out"][none_local] == 0)
+    _say(f"   ok: aq code diffs {nd}, scale diffs {ns}, out cond {n1}, uncond {n2:.2e}")
+    return res
+
+
+@pytest.mark.parametrize("path", ["auto", "small_m", "staged", "large_m"])
+def test_tiny_all_paths(path):
+    res = _full_check(synth.make(0), path)
+    assert res["chosen"] == ("small_m" if path == "auto" else path)
+
+
+def test_mid_remote_pairs_and_ragged_tiles():
+    # 200 tokens (ragged against 64-token chunks and 16-token tiles), half the
+    # slots remote, ~50 rows per slot (several token tiles)
+    _full_check(synth.make_custom(T=200, H=512, F=256, E=16, k=4, P_local=8, p0=4, seed=11))
+
+
+def test_odd_widths_and_eplb_replicas():
+    # H/128 = 3 and F/128 = 3 (one 32-block group per lane, partial 256-row block
+    # of H), replicas over 2 ranks, a non-zero global token id base
+    _full_check(synth.make_custom(T=300, H=384, F=384, E=12, k=3, P_local=8, p0=8, redundant=4, ranks=2,
+                                  seed=12, token_id_base=123456))
+
+
+def test_wide_k_and_many_experts():
+    # k = 16 of 1024 experts (16 logits per lane), skewed popularity
+    _full_check(synth.make_custom(T=96, H=256, F=128, E=1024, k=16, P_local=64, p0=0, seed=13, zipf_s=1.2))
+
+
+def test_single_token_and_capacity_bucket():
+    wl = synth.make_custom(T=1, H=256, F=128, E=8, k=2, P_local=8, seed=14, T_max=512)
+    _full_check(wl)
+
+
+def test_all_pairs_remote_gives_zero_output():
+    wl = synth.make_custom(T=40, H=256, F=128, E=16, k=2, P_local=4, p0=12, seed=15)
+    wl.logits[:, 12:] = -30.0          # nobody picks experts 12..15
+    res = _full_check(wl)
+    assert res["rows"] == 0 and np.all(res["out"] == 0)
+
+
+def test_zero_tokens_writes_nothing():
+    wl = synth.make_custom(T=0, H=256, F=128, E=8, k=2, P_local=8, seed=16, T_max=64)
+    d = mx.Dims.of(wl.dims)
+    buf = P.upload(synth.make_custom(T=1, H=256, F=128, E=8, k=2, P_local=8, seed=16))
+    out = torch.full((4, d.H), 7, dtype=torch.int16, device="cuda")
+    hist = torch.zeros(d.P_total, dtype=torch.int32, device="cuda")
+    mx.moe_forward(d, buf["x"], buf["logits"], buf["w1"], buf["w1s"], buf["w2"], buf["w2s"], buf["rep_count"],
+                   buf["rep_slots"], out, mx.workspace(d), load_hist=hist)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7) and torch.all(hist == 0)
+
+
+def test_component_calls_match_forward_bitwise():
+    wl = synth.make_custom(T=130, H=512, F=256, E=16, k=4, P_local=8, p0=4, redundant=8, ranks=2, seed=17)
+    d = mx.Dims.of(wl.dims)
+    buf = P.upload(wl)
+    res = P.run_forward(wl, buf=buf)
+    TK, TMK = d.T * d.k, d.T_max * d.k
+    z = lambda n, dt: torch.zeros(n, dtype=dt, device="cuda")  # noqa: E731
+    ids, w, phys = z(TK, torch.int32), z(TK, torch.float32), z(TK, torch.int32)
+    hist = z(d.P_total, torch.int32)
+    counts, offsets = z(d.P_local, torch.int32), z(d.P_local + 1, torch.int32)
+    rop, por = z(TK, torch.int32), z(TMK, torch.int32)
+    xq, xs = z(TMK * d.H, torch.uint8), z(TMK * d.H // 128, torch.uint8)
+    aq, as_ = z(TMK * d.F, torch.uint8), z(TMK * d.F // 128, torch.uint8)
+    out = torch.full((d.T, d.H), -1, dtype=torch.int16, device="cuda")
+    ws = mx.workspace(d)
+    mx.moe_route(d, buf["logits"], ids, w)
+    mx.moe_eplb_remap_record(d, ids, buf["rep_count"], buf["rep_slots"], phys, hist, ws)
+    mx.moe_quant_permute(d, buf["x"], phys, xq, xs, counts, offsets, rop, por, ws)
+    mx.moe_grouped_gemm1_swiglu(d, xq, xs, offsets, buf["w1"], buf["w1s"], aq, as_, ws)
+    mx.moe_grouped_gemm2_combine(d, aq, as_, offsets, buf["w2"], buf["w2s"], rop, w, out, ws)
+    torch.cuda.synchronize()
+    rows = res["rows"]
+    assert np.array_equal(ids.cpu().numpy().reshape(d.T, d.k), res["topk_ids"])
+    assert np.array_equal(w.cpu().numpy().reshape(d.T, d.k), res["topk_w"])
+    assert np.array_equal(phys.cpu().numpy().reshape(d.T, d.k), res["phys_ids"])
+    assert np.array_equal(hist.cpu().numpy(), res["hist"])
+    assert np.array_equal(offsets.cpu().numpy(), res["offsets"])
+    assert np.array_equal(por.cpu().numpy()[:rows], res["pair_of_row"])
+    assert np.array_equal(aq.cpu().numpy()[:rows * d.F].reshape(rows, d.F), res["aq"])
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), res["out"])
+
+
+def test_deterministic_and_histogram_accumulates():
+    wl = synth.make_custom(T=257, H=256, F=128, E=32, k=6, P_local=16, p0=8, redundant=8, ranks=2, seed=18)
+    d = mx.Dims.of(wl.dims)
+    buf = P.upload(wl)
+    hist = torch.zeros(d.P_total, dtype=torch.int32, device="cuda")
+    a = P.run_forward(wl, buf=buf, hist_init=hist)
+    b = P.run_forward(wl, buf=buf, hist_init=hist)
+    for n in ("out", "topk_w", "aq", "as_", "xq", "pair_of_row"):
+        assert np.array_equal(a[n], b[n]), n
+    ref = P.oracle_front(wl)
+    assert np.array_equal(hist.cpu().numpy(), 2 * ref["load_hist"])
+    assert hist.cpu().numpy().sum() == 2 * d.T * d.k
+
+
+def test_quant_every_bf16_value():
+    """Every finite bf16 pattern goes through the activation quantiser."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]
+    H = 1024
+    T = (bits.size + H - 1) // H
+    x = np.zeros(T * H, np.uint16)
+    x[:bits.size] = bits
+    rng = np.random.default_rng(0)
+    x = x[rng.permutation(x.size)].reshape(T, H)   # mix magnitudes inside blocks
+    wl = synth.make_custom(T=T, H=H, F=128, E=4, k=1, P_local=4, seed=19)
+    wl.x = x
+    d = mx.Dims.of(wl.dims)
+    buf = P.upload(wl)
+    ids = torch.zeros(T, dtype=torch.int32, device="cuda")    # every token to expert 0
+    rop, por = torch.zeros(T, dtype=torch.int32, device="cuda"), torch.zeros(T, dtype=torch.int32, device="cuda")
+    xq = torch.zeros(T * H, dtype=torch.uint8, device="cuda")
+    xs = torch.zeros(T * H // 128, dtype=torch.uint8, device="cuda")
+    counts = torch.zeros(4, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(5, dtype=torch.int32, device="cuda")
+    mx.moe_quant_permute(d, buf["x"], ids, xq, xs, counts, offsets, rop, por, mx.workspace(d))
+    torch.cuda.synchronize()
+    q, s = om.quant_blocks(fm.bf16_to_f64(x))
+    assert np.array_equal(xs.cpu().numpy().reshape(T, -1), s)
+    assert np.array_equal(xq.cpu().numpy().reshape(T, H), q)
+
+
+# ---------------------------------------------------------------------------- full size
+
+def _big_check(wl, n_slots=3, n_tokens=24, path="auto"):
+    d = wl.dims
+    _say(f"[case] {wl.name} T={d.T} path={path}")
+    res = P.run_forward(wl, path=path)
+    ref = P.oracle_front(wl)
+    P.check_front(res, ref, d)
+    rng = np.random.default_rng(d.T)
+    toks = np.sort(rng.choice(d.T, size=min(n_tokens, d.T), replace=False))
+    rop = ref["row_of_pair"].reshape(d.T, d.k)
+    slots = set(rng.choice(d.P_local, size=n_slots, replace=False).tolist())
+    for t in toks:
+        for j in range(d.k):
+            if rop[t, j] >= 0:
+                slots.add(int(ref["phys_ids"][t, j]) - d.p0)
+    y_c, (nd, ns) = P.expert_check(wl, res, ref, sorted(slots))
+    cond = P.conditioned_out(toks, ref, y_c, d)
+    n1 = P.check_out(res["out"][toks], cond, "conditioned")
+    unc = np.stack([om.forward_token(wl, int(t)) for t in toks[:8]])
+    n2, _ = P.rel_errors(fm.bf16_to_f64(res["out"][toks[:8]]), unc)
+    assert n2 <= P.OUT_NORM_TOL
+    _say(f"   ok: {len(slots)} slots, aq code diffs {nd}, scale diffs {ns}, out cond {n1}, uncond {n2:.2e}")
+    return res
+
+
+def test_decode_share_512_tokens():
+    res = _big_check(synth.make(1))
+    assert res["chosen"] == "small_m"
+
+
+def test_prefill_share_8192_tokens():
+    res = _big_check(synth.make(2))
+    assert res["chosen"] == "large_m"
+
+
+def test_skewed_routing_with_eplb_8192_tokens():
+    wl = synth.make(3)
+    res = _big_check(wl)
+    # the recorder saw every pair, on all 448 physical slots
+    assert res["hist"].sum() == wl.dims.T * wl.dims.k and wl.dims.P_total == 448
