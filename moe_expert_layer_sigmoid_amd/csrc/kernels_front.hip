@@ -110,22 +110,26 @@ __global__ __launch_bounds__(256) void k_count(int T, int k, const int32_t* __re
                                                uint32_t token_id_base, int32_t* __restrict__ phys, int do_remap,
                                                int P_total, int p0, int P_local, int32_t* __restrict__ partial,
                                                int32_t* __restrict__ rank) {
-  __shared__ int s_phys[kChunkTokens * 16];
+  __shared__ int4 s_phys4[kChunkTokens * 16 / 4];
+  int* s_phys = reinterpret_cast<int*>(s_phys4);
   const int c = blockIdx.x;
   const int t0 = c * kChunkTokens;
   const int nt = min(kChunkTokens, T - t0);
   const int np = nt * k;
+  const int np4 = (np + 3) / 4;
   const size_t pr0 = (size_t)t0 * k;
-  for (int i = threadIdx.x; i < np; i += blockDim.x) {
-    int p;
-    if (do_remap) {
-      int e = ids[pr0 + i];
-      uint32_t h = fmix32(token_id_base + (uint32_t)(t0 + i / k));
-      int r = (int)(h % (uint32_t)rep_count[e]);
-      p = rep_slots[(size_t)e * R_max + r];
-      phys[pr0 + i] = p;
-    } else {
-      p = phys[pr0 + i];
+  for (int i = threadIdx.x; i < np4 * 4; i += blockDim.x) {
+    int p = -1;  // padding never matches a slot
+    if (i < np) {
+      if (do_remap) {
+        int e = ids[pr0 + i];
+        uint32_t h = fmix32(token_id_base + (uint32_t)(t0 + i / k));
+        int r = (int)(h % (uint32_t)rep_count[e]);
+        p = rep_slots[(size_t)e * R_max + r];
+        phys[pr0 + i] = p;
+      } else {
+        p = phys[pr0 + i];
+      }
     }
     s_phys[i] = p;
   }
@@ -133,7 +137,11 @@ __global__ __launch_bounds__(256) void k_count(int T, int k, const int32_t* __re
   if (partial) {
     for (int q = threadIdx.x; q < P_total; q += blockDim.x) {
       int cnt = 0;
-      for (int i = 0; i < np; ++i) cnt += (s_phys[i] == q) ? 1 : 0;
+#pragma unroll 8
+      for (int i = 0; i < np4; ++i) {
+        const int4 v = s_phys4[i];  // same address in every lane: a broadcast
+        cnt += (v.x == q) + (v.y == q) + (v.z == q) + (v.w == q);
+      }
       partial[(size_t)c * P_total + q] = cnt;
     }
   }
@@ -141,8 +149,12 @@ __global__ __launch_bounds__(256) void k_count(int T, int k, const int32_t* __re
     for (int s = threadIdx.x; s < P_local; s += blockDim.x) {
       const int q = p0 + s;
       int r = 0;
-      for (int i = 0; i < np; ++i) {
-        if (s_phys[i] == q) rank[pr0 + i] = r++;
+      for (int i = 0; i < np4; ++i) {
+        const int4 v = s_phys4[i];
+        if (v.x == q) rank[pr0 + 4 * i] = r++;
+        if (v.y == q) rank[pr0 + 4 * i + 1] = r++;
+        if (v.z == q) rank[pr0 + 4 * i + 2] = r++;
+        if (v.w == q) rank[pr0 + 4 * i + 3] = r++;
       }
     }
   }
@@ -234,9 +246,10 @@ hipError_t launch_scan(int nch, int P_total, int p0, int P_local, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// a3 (part 3) + a4: one wavefront per token.  Lanes j < k resolve the row of
-// pair (t, j) (base of its chunk and slot + rank), then the wave quantises the
-// token: 16 lanes per 128-column block, 8 bf16 per lane; the block amax gives
+// a3 (part 3) + a4: one wavefront per (token, 512-column chunk).  Lanes j < k
+// resolve the row of pair (t, j) (base of its chunk and slot + rank; the
+// chunk-0 wave also writes the row maps), then the wave quantises its four
+// 128-column blocks: 16 lanes per block, 8 bf16 per lane; the block amax gives
 // the e8m0 exponent, codes are RNE e4m3fn of x * 2^-e; the same bytes go to
 // every local row of the token.
 // ---------------------------------------------------------------------------
@@ -246,7 +259,10 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
                                                uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                int32_t* __restrict__ row_of_pair, int32_t* __restrict__ pair_of_row) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nb = H / kActBlock;
+  const int nc = (nb + 3) / 4;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = wid / nc, ch = wid - t * nc;
   if (t >= T) return;  // wave-uniform
   int myrow = -1;
   if (lane < k) {
@@ -255,9 +271,9 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
     if (p >= p0 && p < p0 + P_local) {
       const int s = p - p0;
       myrow = base[(size_t)(t / kChunkTokens) * P_local + s] + rank[pr];
-      pair_of_row[myrow] = (int32_t)pr;
+      if (ch == 0) pair_of_row[myrow] = (int32_t)pr;
     }
-    row_of_pair[pr] = myrow;
+    if (ch == 0) row_of_pair[pr] = myrow;
   }
   int rows[16];
   bool any = false;
@@ -268,42 +284,38 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
     any |= rows[j] >= 0;
   }
   if (!any) return;
-  const int nb = H / kActBlock;
+  const int b = ch * 4 + (lane >> 4);
+  const bool ok = b < nb;
   const int sub = lane & 15;  // 8 columns each
-  const uint16_t* xr = x + (size_t)t * H;
-  for (int b0 = 0; b0 < nb; b0 += 4) {
-    const int b = b0 + (lane >> 4);
-    const bool ok = b < nb;
-    float v[8];
-    if (ok) {
-      uint4 raw = *reinterpret_cast<const uint4*>(xr + b * kActBlock + sub * 8);
-      uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+  if (ok) {
+    uint4 raw = *reinterpret_cast<const uint4*>(x + (size_t)t * H + b * kActBlock + sub * 8);
+    uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(wd[i] << 16);
-        v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(wd[i] << 16);
+      v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
     }
-    float am = 0.0f;
+  } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float am = 0.0f;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
-    const int e = scale_exp(am);
-    uint2 q;
-    q.x = pack4_fp8(ldexpf(v[0], -e), ldexpf(v[1], -e), ldexpf(v[2], -e), ldexpf(v[3], -e));
-    q.y = pack4_fp8(ldexpf(v[4], -e), ldexpf(v[5], -e), ldexpf(v[6], -e), ldexpf(v[7], -e));
-    if (ok) {
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (rows[j] < 0) continue;  // wave-uniform
-        const size_t r = (size_t)rows[j];
-        *reinterpret_cast<uint2*>(xq + r * H + b * kActBlock + sub * 8) = q;
-        if (sub == 0) xs[r * nb + b] = (uint8_t)(e + 127);
-      }
+  for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+  const int e = scale_exp(am);
+  uint2 q;
+  q.x = pack4_fp8(ldexpf(v[0], -e), ldexpf(v[1], -e), ldexpf(v[2], -e), ldexpf(v[3], -e));
+  q.y = pack4_fp8(ldexpf(v[4], -e), ldexpf(v[5], -e), ldexpf(v[6], -e), ldexpf(v[7], -e));
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (rows[j] < 0) continue;  // wave-uniform
+      const size_t r = (size_t)rows[j];
+      *reinterpret_cast<uint2*>(xq + r * H + b * kActBlock + sub * 8) = q;
+      if (sub == 0) xs[r * nb + b] = (uint8_t)(e + 127);
     }
   }
 }
@@ -312,19 +324,25 @@ hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* p
                         const int32_t* base, const int32_t* rank, uint8_t* xq, uint8_t* xs, int32_t* row_of_pair,
                         int32_t* pair_of_row, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  k_quant<<<(T + 3) / 4, 256, 0, st>>>(T, H, k, x, phys, p0, P_local, base, rank, xq, xs, row_of_pair, pair_of_row);
+  const int nc = (H / kActBlock + 3) / 4;
+  const long waves = (long)T * nc;
+  k_quant<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, x, phys, p0, P_local, base, rank, xq, xs,
+                                                       row_of_pair, pair_of_row);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// a7 combine: one wavefront per token; out[t] = sum over local j ascending of
-// w[t][j] * y[row(t, j)] (f32 fma chain), rounded to bf16 (nearest even).
+// a7 combine: one wavefront per (token, 512-column chunk), 8 columns per lane;
+// out[t] = sum over local j ascending of w[t][j] * y[row(t, j)] (f32 fma
+// chain), rounded to bf16 (nearest even).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const float* __restrict__ y,
                                                  const int32_t* __restrict__ row_of_pair,
                                                  const float* __restrict__ w, uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nc = (H + 511) / 512;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = wid / nc, ch = wid - t * nc;
   if (t >= T) return;
   int myrow = -1;
   float myw = 0.0f;
@@ -340,29 +358,39 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
     ws[j] = __shfl(myw, j);
     rows[j] = j < k ? r : -1;
   }
-  uint16_t* orow = out + (size_t)t * H;
-  for (int h = lane * 4; h < H; h += 256) {
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  const int h = ch * 512 + lane * 8;
+  if (h >= H) return;
+  float a[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (rows[j] < 0) continue;  // wave-uniform
-      float4 yv = *reinterpret_cast<const float4*>(y + (size_t)rows[j] * H + h);
-      a0 = fmaf(ws[j], yv.x, a0);
-      a1 = fmaf(ws[j], yv.y, a1);
-      a2 = fmaf(ws[j], yv.z, a2);
-      a3 = fmaf(ws[j], yv.w, a3);
-    }
-    uint2 o;
-    o.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
-    o.y = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
-    *reinterpret_cast<uint2*>(orow + h) = o;
+  for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (rows[j] < 0) continue;  // wave-uniform
+    const float* yr = y + (size_t)rows[j] * H + h;
+    const float4 y0 = *reinterpret_cast<const float4*>(yr);
+    const float4 y1 = *reinterpret_cast<const float4*>(yr + 4);
+    a[0] = fmaf(ws[j], y0.x, a[0]);
+    a[1] = fmaf(ws[j], y0.y, a[1]);
+    a[2] = fmaf(ws[j], y0.z, a[2]);
+    a[3] = fmaf(ws[j], y0.w, a[3]);
+    a[4] = fmaf(ws[j], y1.x, a[4]);
+    a[5] = fmaf(ws[j], y1.y, a[5]);
+    a[6] = fmaf(ws[j], y1.z, a[6]);
+    a[7] = fmaf(ws[j], y1.w, a[7]);
   }
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(a[4]) | ((uint32_t)f32_to_bf16(a[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(a[6]) | ((uint32_t)f32_to_bf16(a[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * H + h) = o;
 }
 
 hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* row_of_pair, const float* w,
                           uint16_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  k_combine<<<(T + 3) / 4, 256, 0, st>>>(T, H, k, y, row_of_pair, w, out);
+  const long waves = (long)T * ((H + 511) / 512);
+  k_combine<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, y, row_of_pair, w, out);
   return hipGetLastError();
 }
 

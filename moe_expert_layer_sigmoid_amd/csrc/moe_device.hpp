@@ -70,6 +70,27 @@ __device__ __forceinline__ int xcd_item(int b, int nblk) {
   return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
+// Buffer resource of `bytes` bytes at `p` (gfx9 descriptor word 3: raw
+// 32-bit dwords, no swizzle).  Buffer loads address it as base + lane offset
+// (VGPR) + uniform offset (SGPR) + immediate, and return 0 outside
+// [0, bytes) instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ int buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ int buf_load2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ int buf_load1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
 // Block-scaled 16x16x128 MFMA, A = MXFP4 (e2m1, 32 K-elements in the 4 low
 // dwords of each lane), B = fp8 e4m3fn, f32 accumulate.  Lane l supplies
 // row/column l % 16 and scale block l / 16; `OPSEL_A` picks the byte of
