@@ -26,7 +26,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, published
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = ("moe_expert_layer_sigmoid_amd/csrc/kernels_gemm.hip",
-                "moe_expert_layer_sigmoid_amd/csrc/moe_device.hpp")
+                "moe_expert_layer_sigmoid_amd/csrc/moe_device.hpp",
+                "moe_expert_layer_sigmoid_amd/csrc/moe_layout.hpp")
 
 
 def _src_hash(paths) -> str:
@@ -69,7 +70,9 @@ def run_gpu(cfg: int, steps: int, warmup: int, copies: int):
     logits = torch.from_numpy(wl.logits).to(dev)
     rc = torch.from_numpy(wl.rep_count).to(dev)
     rs = torch.from_numpy(wl.rep_slots).to(dev)
-    w = [tuple(torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s))]
+    nat = [torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
+    w = [mx.pack_weights(d, *nat)]     # one-time repack, outside the timed region
+    del nat
     for _ in range(copies - 1):
         w.append(tuple(t.clone() for t in w[0]))
     out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)

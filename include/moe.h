@@ -40,11 +40,18 @@
  * Layouts (row-major, C order):
  *  logits   f32  [T, E]
  *  x        bf16 [T, H]                 (uint16 bit patterns)
- *  w1       u8   [P_local, 2F, H/2]     e2m1 pairs, element 2i in the low nibble;
- *                                       rows [0, F) gate, [F, 2F) up
+ *  w1       u8   [P_local, 2F, H/2]     MXFP4: e2m1 pairs, element 2i in the low
+ *                                       nibble; rows [0, F) gate, [F, 2F) up
  *  w1s      u8   [P_local, 2F, H/32]    e8m0 scale of each 32-element block along K
  *  w2       u8   [P_local, H, F/2]
  *  w2s      u8   [P_local, H, F/32]
+ *  pw1, pw1s, pw2, pw2s                 the same weights repacked by
+ *                                       moe_pack_weights (sizes: moe_packed_bytes):
+ *    each 16-row tile, each 256-wide K step, each of the step's two
+ *    16x16x128 MFMAs: 64 lanes x 16 bytes, lane 16g + r holding row r,
+ *    32-block 8 step + 4 i + g; scales per tile and 4 steps: 64 lanes x 8
+ *    bytes, byte 2 (step % 4) + i of lane 16g + r = scale of row r, block
+ *    8 step + 4 i + g.  K is padded with zero blocks to a multiple of 1024.
  *  rep_count  i32 [E]                   replicas of each logical expert (>= 1)
  *  rep_slots  i32 [E, R_max]            physical slot of replica r of expert e
  *  load_hist  i32 [P_total]             += pairs per physical slot (nullable)
@@ -124,6 +131,20 @@ moe_path_t moe_select_path(const moe_dims_t* dims);
 /* Static text for a status code. */
 const char* moe_status_string(int status);
 
+/* Bytes of a packed weight buffer for `dims` over all P_local slots:
+ * which = 0 pw1, 1 pw1s, 2 pw2, 3 pw2s.  Returns 0 for invalid arguments. */
+size_t moe_packed_bytes(const moe_dims_t* dims, int which);
+
+/* Repack MXFP4 expert weights (natural layout above) into the MFMA-operand
+ * order the GEMM kernels stream: every weight load of a wavefront becomes one
+ * contiguous 1 KB and one 8-byte scale load covers four K steps of a tile.
+ * Pure byte movement, run once when weights are loaded (like the checkpoint
+ * conversion that produced the MXFP4 experts [InferenceX PR 3430, Additional
+ * detail section]).  Output buffers must not overlap the inputs. */
+int moe_pack_weights(const moe_dims_t* dims, const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
+                     const uint8_t* w2s, uint8_t* pw1, uint8_t* pw1s, uint8_t* pw2, uint8_t* pw2s,
+                     moe_stream_t stream);
+
 /* a1. Top-k routing [sglang PR 35619, "Four settings that silently break it"].
  * For each token: the k largest logits (descending, equal logits to the lower
  * expert id); weight_j = sigmoid(l_j) / sum_i sigmoid(l_i) in f32. */
@@ -153,9 +174,10 @@ int moe_quant_permute(const moe_dims_t* dims, const uint16_t* x, const int32_t* 
 /* a5. GEMM1 + SwiGLU + fp8 requant, grouped by slot [sglang PR 47065, intro].
  * For each row r of slot s: h = W1_s a_r (f32 accumulation of block-scaled
  * fp8 x MXFP4 products); act_f = silu(h_f) * h_{F+f}; act requantised with
- * the a4 rule per 128 columns into aq / as.  `offsets` as from a3. */
+ * the a4 rule per 128 columns into aq / as.  `offsets` as from a3; weights
+ * packed by moe_pack_weights. */
 int moe_grouped_gemm1_swiglu(const moe_dims_t* dims, const uint8_t* xq, const uint8_t* xs,
-                             const int32_t* offsets, const uint8_t* w1, const uint8_t* w1s,
+                             const int32_t* offsets, const uint8_t* pw1, const uint8_t* pw1s,
                              uint8_t* aq, uint8_t* as, void* workspace, size_t workspace_bytes,
                              moe_stream_t stream);
 
@@ -163,7 +185,7 @@ int moe_grouped_gemm1_swiglu(const moe_dims_t* dims, const uint8_t* xq, const ui
  * y_r = W2_s dequant(aq_r) (f32); out[t] = bf16_rne(sum over local j, ascending,
  * of topk_w[t][j] * y[row_of_pair[t*k+j]]); tokens with no local pair get +0. */
 int moe_grouped_gemm2_combine(const moe_dims_t* dims, const uint8_t* aq, const uint8_t* as,
-                              const int32_t* offsets, const uint8_t* w2, const uint8_t* w2s,
+                              const int32_t* offsets, const uint8_t* pw2, const uint8_t* pw2s,
                               const int32_t* row_of_pair, const float* topk_w, uint16_t* out,
                               void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
@@ -174,7 +196,7 @@ int moe_grouped_gemm2_combine(const moe_dims_t* dims, const uint8_t* aq, const u
  * taken.  `taps` (host struct of device pointers, nullable) receives copies
  * of the intermediates. */
 int moe_forward(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, const float* logits,
-                const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2, const uint8_t* w2s,
+                const uint8_t* pw1, const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s,
                 const int32_t* rep_count, const int32_t* rep_slots, int32_t* load_hist,
                 uint16_t* out, const moe_taps_t* taps, moe_path_t* chosen,
                 void* workspace, size_t workspace_bytes, moe_stream_t stream);

@@ -24,7 +24,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspac
 PATHS = {"auto": 0, "small_m": 1, "staged": 2, "large_m": 3}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
-EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_route",
+EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_packed_bytes",
+           "moe_pack_weights", "moe_route",
            "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
            "moe_grouped_gemm2_combine", "moe_forward")
 
@@ -77,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.moe_select_path.restype = I
         L.moe_status_string.argtypes = [I]
         L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_packed_bytes.argtypes = [D, I]
+        L.moe_packed_bytes.restype = ctypes.c_size_t
+        L.moe_pack_weights.argtypes = [D, P, P, P, P, P, P, P, P, P]
         L.moe_route.argtypes = [D, P, P, P, P]
         L.moe_eplb_remap_record.argtypes = [D, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_quant_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -84,7 +88,7 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gemm2_combine.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_forward.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps),
                                   ctypes.POINTER(ctypes.c_int), P, ctypes.c_size_t, P]
-        for n in ("moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
+        for n in ("moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
                   "moe_grouped_gemm2_combine", "moe_forward"):
             getattr(L, n).restype = I
         _lib_handle = L
@@ -152,6 +156,29 @@ def moe_status_string(code: int) -> str:
     return lib().moe_status_string(int(code)).decode()
 
 
+def moe_packed_bytes(d: Dims, which: int) -> int:
+    return int(lib().moe_packed_bytes(ctypes.byref(d), int(which)))
+
+
+def moe_pack_weights(d: Dims, w1, w1s, w2, w2s, pw1, pw1s, pw2, pw2s, stream=None):
+    nw1, ns1 = d.P_local * 2 * d.F * d.H // 2, d.P_local * 2 * d.F * d.H // 32
+    nw2, ns2 = d.P_local * d.H * d.F // 2, d.P_local * d.H * d.F // 32
+    rc = lib().moe_pack_weights(
+        ctypes.byref(d), _ptr(w1, "w1", u8, nw1), _ptr(w1s, "w1s", u8, ns1), _ptr(w2, "w2", u8, nw2),
+        _ptr(w2s, "w2s", u8, ns2), _ptr(pw1, "pw1", u8, moe_packed_bytes(d, 0)),
+        _ptr(pw1s, "pw1s", u8, moe_packed_bytes(d, 1)), _ptr(pw2, "pw2", u8, moe_packed_bytes(d, 2)),
+        _ptr(pw2s, "pw2s", u8, moe_packed_bytes(d, 3)), _stream(stream))
+    _check("moe_pack_weights", rc)
+
+
+def pack_weights(d: Dims, w1, w1s, w2, w2s, stream=None):
+    """Allocate and fill the packed weight buffers; returns (pw1, pw1s, pw2, pw2s)."""
+    dev = w1.device
+    out = tuple(torch.empty(moe_packed_bytes(d, i), dtype=u8, device=dev) for i in range(4))
+    moe_pack_weights(d, w1, w1s, w2, w2s, *out, stream=stream)
+    return out
+
+
 def workspace(d: Dims, device="cuda") -> torch.Tensor:
     """A workspace of moe_workspace_bytes(d) bytes (torch-allocated, 256-B aligned)."""
     n = moe_workspace_bytes(d)
@@ -185,23 +212,23 @@ def moe_quant_permute(d: Dims, x, phys_ids, xq, xs, counts, offsets, row_of_pair
     _check("moe_quant_permute", rc)
 
 
-def moe_grouped_gemm1_swiglu(d: Dims, xq, xs, offsets, w1, w1s, aq, as_, ws, stream=None):
+def moe_grouped_gemm1_swiglu(d: Dims, xq, xs, offsets, pw1, pw1s, aq, as_, ws, stream=None):
     _, TMK = _sizes(d)
     rc = lib().moe_grouped_gemm1_swiglu(
         ctypes.byref(d), _ptr(xq, "xq", u8, TMK * d.H), _ptr(xs, "xs", u8, TMK * (d.H // 128)),
         _ptr(offsets, "offsets", i32, d.P_local + 1),
-        _ptr(w1, "w1", u8, d.P_local * 2 * d.F * d.H // 2), _ptr(w1s, "w1s", u8, d.P_local * 2 * d.F * d.H // 32),
+        _ptr(pw1, "pw1", u8, moe_packed_bytes(d, 0)), _ptr(pw1s, "pw1s", u8, moe_packed_bytes(d, 1)),
         _ptr(aq, "aq", u8, TMK * d.F), _ptr(as_, "as", u8, TMK * (d.F // 128)),
         _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
     _check("moe_grouped_gemm1_swiglu", rc)
 
 
-def moe_grouped_gemm2_combine(d: Dims, aq, as_, offsets, w2, w2s, row_of_pair, topk_w, out, ws, stream=None):
+def moe_grouped_gemm2_combine(d: Dims, aq, as_, offsets, pw2, pw2s, row_of_pair, topk_w, out, ws, stream=None):
     TK, TMK = _sizes(d)
     rc = lib().moe_grouped_gemm2_combine(
         ctypes.byref(d), _ptr(aq, "aq", u8, TMK * d.F), _ptr(as_, "as", u8, TMK * (d.F // 128)),
         _ptr(offsets, "offsets", i32, d.P_local + 1),
-        _ptr(w2, "w2", u8, d.P_local * d.H * d.F // 2), _ptr(w2s, "w2s", u8, d.P_local * d.H * d.F // 32),
+        _ptr(pw2, "pw2", u8, moe_packed_bytes(d, 2)), _ptr(pw2s, "pw2s", u8, moe_packed_bytes(d, 3)),
         _ptr(row_of_pair, "row_of_pair", i32, TK), _ptr(topk_w, "topk_w", f32, TK),
         _ptr(out, "out", _bf16(out), d.T * d.H), _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
     _check("moe_grouped_gemm2_combine", rc)
@@ -217,9 +244,10 @@ def make_taps(d: Dims, device="cuda") -> Dict[str, torch.Tensor]:
                 as_=z(TMK * (d.F // 128), u8))
 
 
-def moe_forward(d: Dims, x, logits, w1, w1s, w2, w2s, rep_count, rep_slots, out, ws, load_hist=None,
+def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, out, ws, load_hist=None,
                 path: str = "auto", taps: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> str:
-    """Run the whole layer; returns the path taken ("small_m", "staged", "large_m")."""
+    """Run the whole layer on packed weights; returns the path taken
+    ("small_m", "staged", "large_m")."""
     TK, TMK = _sizes(d)
     tp = None
     if taps is not None:
@@ -231,8 +259,8 @@ def moe_forward(d: Dims, x, logits, w1, w1s, w2, w2s, rep_count, rep_slots, out,
     chosen = ctypes.c_int(-1)
     rc = lib().moe_forward(
         ctypes.byref(d), PATHS[path], _ptr(x, "x", _bf16(x), d.T * d.H), _ptr(logits, "logits", f32, d.T * d.E),
-        _ptr(w1, "w1", u8, d.P_local * 2 * d.F * d.H // 2), _ptr(w1s, "w1s", u8, d.P_local * 2 * d.F * d.H // 32),
-        _ptr(w2, "w2", u8, d.P_local * d.H * d.F // 2), _ptr(w2s, "w2s", u8, d.P_local * d.H * d.F // 32),
+        _ptr(pw1, "pw1", u8, moe_packed_bytes(d, 0)), _ptr(pw1s, "pw1s", u8, moe_packed_bytes(d, 1)),
+        _ptr(pw2, "pw2", u8, moe_packed_bytes(d, 2)), _ptr(pw2s, "pw2s", u8, moe_packed_bytes(d, 3)),
         _ptr(rep_count, "rep_count", i32, d.E), _ptr(rep_slots, "rep_slots", i32, d.E * d.R_max),
         _ptr(load_hist, "load_hist", i32, d.P_total), _ptr(out, "out", _bf16(out), d.T * d.H),
         ctypes.byref(tp) if tp is not None else None, ctypes.byref(chosen),

@@ -6,6 +6,7 @@
 #include "../../include/moe.h"
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
+#include "moe_layout.hpp"
 
 using namespace moe;
 
@@ -110,6 +111,31 @@ moe_path_t moe_select_path(const moe_dims_t* d) {
   return MOE_PATH_STAGED;
 }
 
+size_t moe_packed_bytes(const moe_dims_t* d, int which) {
+  if (check_dims(d) != MOE_OK) return 0;
+  const PackGeom g1 = pack_geom(2u * d->F, (uint32_t)d->H), g2 = pack_geom((uint32_t)d->H, (uint32_t)d->F);
+  switch (which) {
+    case 0: return g1.data_slot * d->P_local;
+    case 1: return g1.scale_slot * d->P_local;
+    case 2: return g2.data_slot * d->P_local;
+    case 3: return g2.scale_slot * d->P_local;
+    default: return 0;
+  }
+}
+
+int moe_pack_weights(const moe_dims_t* d, const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2, const uint8_t* w2s,
+                     uint8_t* pw1, uint8_t* pw1s, uint8_t* pw2, uint8_t* pw2s, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  const void* ps[] = {w1, w1s, w2, w2s, pw1, pw1s, pw2, pw2s};
+  for (const void* p : ps)
+    if (!dev_ok(p)) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY(launch_pack(w1, w1s, pw1, pw1s, d->P_local, 2 * d->F, d->H, st));
+  MOE_TRY(launch_pack(w2, w2s, pw2, pw2s, d->P_local, d->H, d->F, st));
+  return MOE_OK;
+}
+
 const char* moe_status_string(int s) {
   switch (s) {
     case MOE_OK: return "ok";
@@ -173,24 +199,24 @@ int moe_quant_permute(const moe_dims_t* d, const uint16_t* x, const int32_t* phy
 }
 
 int moe_grouped_gemm1_swiglu(const moe_dims_t* d, const uint8_t* xq, const uint8_t* xs, const int32_t* offsets,
-                             const uint8_t* w1, const uint8_t* w1s, uint8_t* aq, uint8_t* as, void* ws,
+                             const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, void* ws,
                              size_t ws_bytes, moe_stream_t stream) {
   int rc = check_dims(d);
   if (rc) return rc;
-  if (!dev_ok(xq) || !dev_ok(xs) || !dev_ok(offsets) || !dev_ok(w1) || !dev_ok(w1s) || !dev_ok(aq) || !dev_ok(as))
+  if (!dev_ok(xq) || !dev_ok(xs) || !dev_ok(offsets) || !dev_ok(pw1) || !dev_ok(pw1s) || !dev_ok(aq) || !dev_ok(as))
     return MOE_ERR_INVALID_ARG;
   if ((rc = check_ws(d, ws, ws_bytes))) return rc;
   if (d->T == 0) return MOE_OK;
-  return hip_status(launch_gemm1_stream(xq, xs, offsets, w1, w1s, aq, as, d->H, d->F, d->P_local,
+  return hip_status(launch_gemm1_stream(xq, xs, offsets, pw1, pw1s, aq, as, d->H, d->F, d->P_local,
                                         (hipStream_t)stream));
 }
 
 int moe_grouped_gemm2_combine(const moe_dims_t* d, const uint8_t* aq, const uint8_t* as, const int32_t* offsets,
-                              const uint8_t* w2, const uint8_t* w2s, const int32_t* row_of_pair, const float* topk_w,
-                              uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+                              const uint8_t* pw2, const uint8_t* pw2s, const int32_t* row_of_pair,
+                              const float* topk_w, uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   int rc = check_dims(d);
   if (rc) return rc;
-  if (!dev_ok(aq) || !dev_ok(as) || !dev_ok(offsets) || !dev_ok(w2) || !dev_ok(w2s) || !dev_ok(row_of_pair) ||
+  if (!dev_ok(aq) || !dev_ok(as) || !dev_ok(offsets) || !dev_ok(pw2) || !dev_ok(pw2s) || !dev_ok(row_of_pair) ||
       !dev_ok(topk_w) || !dev_ok(out))
     return MOE_ERR_INVALID_ARG;
   if ((rc = check_ws(d, ws, ws_bytes))) return rc;
@@ -198,19 +224,19 @@ int moe_grouped_gemm2_combine(const moe_dims_t* d, const uint8_t* aq, const uint
   hipStream_t st = (hipStream_t)stream;
   Layout L = layout_of(d);
   float* y = at<float>(ws, L.y);
-  MOE_TRY(launch_gemm2_stream(aq, as, offsets, w2, w2s, y, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st));
   MOE_TRY(launch_combine(d->T, d->H, d->k, y, row_of_pair, topk_w, out, st));
   return MOE_OK;
 }
 
-int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const float* logits, const uint8_t* w1,
-                const uint8_t* w1s, const uint8_t* w2, const uint8_t* w2s, const int32_t* rep_count,
+int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const float* logits, const uint8_t* pw1,
+                const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rep_count,
                 const int32_t* rep_slots, int32_t* load_hist, uint16_t* out, const moe_taps_t* taps,
                 moe_path_t* chosen, void* ws, size_t ws_bytes, moe_stream_t stream) {
   int rc = check_dims(d);
   if (rc) return rc;
   if (path < MOE_PATH_AUTO || path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
-  if (!dev_ok(x) || !dev_ok(logits) || !dev_ok(w1) || !dev_ok(w1s) || !dev_ok(w2) || !dev_ok(w2s) ||
+  if (!dev_ok(x) || !dev_ok(logits) || !dev_ok(pw1) || !dev_ok(pw1s) || !dev_ok(pw2) || !dev_ok(pw2s) ||
       !dev_ok(rep_count) || !dev_ok(rep_slots) || !opt_ok(load_hist) || !dev_ok(out))
     return MOE_ERR_INVALID_ARG;
   if (taps) {
@@ -252,8 +278,8 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
                        d->p0, d->P_local, partial, rank, st));
   MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, counts, offsets, base, load_hist, st));
   MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys, d->p0, d->P_local, base, rank, xq, xs, rop, por, st));
-  MOE_TRY(launch_gemm1_stream(xq, xs, offsets, w1, w1s, aq, as, d->H, d->F, d->P_local, st));
-  MOE_TRY(launch_gemm2_stream(aq, as, offsets, w2, w2s, y, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_gemm1_stream(xq, xs, offsets, pw1, pw1s, aq, as, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st));
   MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, st));
   return MOE_OK;
 }

@@ -6,6 +6,7 @@
 
 namespace moe {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -80,6 +81,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 }
 __device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ v2i buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 __device__ __forceinline__ int buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return (int)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);

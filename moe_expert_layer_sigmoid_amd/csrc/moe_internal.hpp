@@ -31,11 +31,15 @@ hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* p
 hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* row_of_pair, const float* w,
                           uint16_t* out, hipStream_t st);
 
-// GEMM kernels (kernels_gemm.hip)
-hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* w1,
-                               const uint8_t* w1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
+// GEMM kernels (kernels_gemm.hip).  Weights are in the packed layout of
+// moe_layout.hpp; launch_pack converts one natural MXFP4 matrix set
+// [P, R, K/2] + [P, R, K/32] into it.
+hipError_t launch_pack(const uint8_t* w, const uint8_t* ws, uint8_t* pw, uint8_t* ps, int P, int R, int K,
+                       hipStream_t st);
+hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
+                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
                                hipStream_t st);
-hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* w2,
-                               const uint8_t* w2s, float* y, int H, int F, int P_local, hipStream_t st);
+hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
+                               const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
 
 }  // namespace moe

@@ -40,8 +40,14 @@ def dev(a: np.ndarray, dtype=None) -> torch.Tensor:
 
 
 def upload(wl) -> dict:
-    return dict(x=dev(wl.x.view(np.int16)), logits=dev(wl.logits), w1=dev(wl.w1), w1s=dev(wl.w1s),
-                w2=dev(wl.w2), w2s=dev(wl.w2s), rep_count=dev(wl.rep_count.astype(np.int32)),
+    """Device copies of a workload; expert weights are packed by the library
+    (moe_pack_weights) into w1..w2s, the natural MXFP4 bytes are not kept."""
+    d = mx.Dims.of(wl.dims)
+    nat = [dev(a) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
+    packed = mx.pack_weights(d, *nat)
+    del nat
+    return dict(x=dev(wl.x.view(np.int16)), logits=dev(wl.logits), w1=packed[0], w1s=packed[1],
+                w2=packed[2], w2s=packed[3], rep_count=dev(wl.rep_count.astype(np.int32)),
                 rep_slots=dev(wl.rep_slots.astype(np.int32)))
 
 
