@@ -93,6 +93,23 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 int nchunks(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
 
+// GEMM kernels of a path: weight streaming for few rows per expert, the
+// persistent tiled kernels for many.
+hipError_t gemm1(moe_path_t p, const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
+                 const uint8_t* pw1s, uint8_t* aq, uint8_t* as, const moe_dims_t* d, hipStream_t st) {
+  if (p == MOE_PATH_LARGE_M) return launch_gemm1_tiled(xq, xs, offsets, pw1, pw1s, aq, as, d->H, d->F, d->P_local, st);
+  return launch_gemm1_stream(xq, xs, offsets, pw1, pw1s, aq, as, d->H, d->F, d->P_local, st);
+}
+hipError_t gemm2(moe_path_t p, const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
+                 const uint8_t* pw2s, float* y, const moe_dims_t* d, hipStream_t st) {
+  if (p == MOE_PATH_LARGE_M) return launch_gemm2_tiled(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st);
+  return launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st);
+}
+// The component GEMM calls pick by token count like MOE_PATH_AUTO.
+moe_path_t gemm_path(const moe_dims_t* d) {
+  return moe_select_path(d) == MOE_PATH_LARGE_M ? MOE_PATH_LARGE_M : MOE_PATH_SMALL_M;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,8 +224,7 @@ int moe_grouped_gemm1_swiglu(const moe_dims_t* d, const uint8_t* xq, const uint8
     return MOE_ERR_INVALID_ARG;
   if ((rc = check_ws(d, ws, ws_bytes))) return rc;
   if (d->T == 0) return MOE_OK;
-  return hip_status(launch_gemm1_stream(xq, xs, offsets, pw1, pw1s, aq, as, d->H, d->F, d->P_local,
-                                        (hipStream_t)stream));
+  return hip_status(gemm1(gemm_path(d), xq, xs, offsets, pw1, pw1s, aq, as, d, (hipStream_t)stream));
 }
 
 int moe_grouped_gemm2_combine(const moe_dims_t* d, const uint8_t* aq, const uint8_t* as, const int32_t* offsets,
@@ -224,7 +240,7 @@ int moe_grouped_gemm2_combine(const moe_dims_t* d, const uint8_t* aq, const uint
   hipStream_t st = (hipStream_t)stream;
   Layout L = layout_of(d);
   float* y = at<float>(ws, L.y);
-  MOE_TRY(launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st));
+  MOE_TRY(gemm2(gemm_path(d), aq, as, offsets, pw2, pw2s, y, d, st));
   MOE_TRY(launch_combine(d->T, d->H, d->k, y, row_of_pair, topk_w, out, st));
   return MOE_OK;
 }
@@ -278,8 +294,8 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
                        d->p0, d->P_local, partial, rank, st));
   MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, counts, offsets, base, load_hist, st));
   MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys, d->p0, d->P_local, base, rank, xq, xs, rop, por, st));
-  MOE_TRY(launch_gemm1_stream(xq, xs, offsets, pw1, pw1s, aq, as, d->H, d->F, d->P_local, st));
-  MOE_TRY(launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st));
+  MOE_TRY(gemm1(p, xq, xs, offsets, pw1, pw1s, aq, as, d, st));
+  MOE_TRY(gemm2(p, aq, as, offsets, pw2, pw2s, y, d, st));
   MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, st));
   return MOE_OK;
 }

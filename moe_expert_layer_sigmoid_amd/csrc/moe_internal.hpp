@@ -41,5 +41,12 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
                                hipStream_t st);
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                                const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
+// Large-M: persistent tiled kernels (grid = one block per CU, items decoded
+// on the device from offsets).
+hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
+                              const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
+                              hipStream_t st);
+hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
+                              const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
 
 }  // namespace moe
