@@ -56,14 +56,14 @@ def layer_bytes(d, touched: int) -> int:
     return w + d.T * (d.E * 4 + d.H * 2 + d.H * 2)
 
 
-def run_gpu(cfg: int, steps: int, warmup: int, copies: int):
+def run_gpu(workload: str, steps: int, warmup: int, copies: int):
     import torch
     import moe_expert_layer_sigmoid_amd as mx
     import synth
 
     t0 = time.time()
-    wl = synth.make(cfg)
-    _log(f"[bench] inputs for cfg{cfg} generated in {time.time() - t0:.1f}s")
+    wl = synth.make(workload)
+    _log(f"[bench] inputs for {workload} generated in {time.time() - t0:.1f}s")
     d = mx.Dims.of(wl.dims)
     dev = "cuda"
     x = torch.from_numpy(wl.x.view("int16")).to(dev)
@@ -158,15 +158,28 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated over steps")
-    ap.add_argument("--cfg", type=int, default=1, help=argparse.SUPPRESS)
+    ap.add_argument("--workload", default="decode512", help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slots", type=int, default=8)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first copy a buffer of this many MiB with torch (a plain copy kernel of "
+                         "known size, for scaling HBM byte counters under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported"}))
         sys.exit(2)
 
-    r = run_gpu(args.cfg, args.steps, args.warmup, args.copies)
+    if args.calibrate_copy_mib:
+        import torch
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        _log(f"[bench] calibration copies: 3 x {n} bytes read and written")
+        del src, dst
+    r = run_gpu(args.workload, args.steps, args.warmup, args.copies)
     d = r["d"]
     ms = r["wall"] * 1000.0 / args.steps
     value = d.T * args.steps / r["wall"]
@@ -195,7 +208,7 @@ def main():
                    "weight_copies": args.copies},
         "roofline": {"bound": "hbm", "kernel": "k_gemm1_stream", "achieved": round(g1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile("k_gemm1_stream", "cfg1"),
+                     "traffic": traffic_from_profile("k_gemm1_stream", args.workload),
                      "bytes_per_launch": g1_bytes, "avg_launch_us": round(r["gemm1_us"], 2)},
         "layer_roofline": {"bound": "hbm", "achieved": round(lay_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(lay_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": lay_bytes,

@@ -462,23 +462,25 @@ __global__ __launch_bounds__(256 * TG, 1) void k_tiled(
       const int t = i / nb, c = i - t * nb;
       S.xs[t * nb + c] = t < nvalid ? xs[(size_t)(r0 + t) * nb + c] : (uint8_t)0;
     }
-    // token stage loader: 16-byte chunks, 8 per token row
+    // token stage loader: 16-byte chunks, 8 per token row; two register sets
+    // so that a stage's rows are loaded three stages before use and written
+    // to LDS one stage before use
     const rsrc_t Xr = make_rsrc(xq + (size_t)r0 * K, (uint32_t)nvalid * K);
-    uint4 breg[4];
-    auto b_load = [&](int stg) {
+    uint4 breg0[4], breg1[4];
+    auto b_load = [&](uint4 (&br)[4], int stg) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = tid + j * 256 * TG;  // chunk: token c / 8, piece c % 8
         const int t = c >> 3, pc = c & 7;
-        breg[j] = __builtin_bit_cast(uint4, buf_load16(Xr, (uint32_t)t * K + pc * 16, (uint32_t)stg * 128));
+        br[j] = __builtin_bit_cast(uint4, buf_load16(Xr, (uint32_t)t * K + pc * 16, (uint32_t)stg * 128));
       }
     };
-    auto b_store = [&](int buf) {
+    auto b_store = [&](const uint4 (&br)[4], int buf) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = tid + j * 256 * TG;
         const int t = c >> 3, pc = c & 7;
-        *reinterpret_cast<uint4*>(&S.b[buf][t * kLPitch + pc * 16]) = breg[j];
+        *reinterpret_cast<uint4*>(&S.b[buf][t * kLPitch + pc * 16]) = br[j];
       }
     };
     v4i a0[4], a1[4];
@@ -499,16 +501,19 @@ __global__ __launch_bounds__(256 * TG, 1) void k_tiled(
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int ngrp = (Gm.steps + 3) / 4 * 0 + Gm.steps / 4;  // scale groups of 8 stages
-    b_load(0);
+    const int ngrp = Gm.steps / 4;  // scale groups of 8 stages
+    // prologue: rows of stages 0 and 1 to LDS, stage 2 in flight; weights of stages 0, 1
+    b_load(breg0, 0);
+    if (nb > 1) b_load(breg1, 1);
     s_loadq(scur, 0);
     s_loadq(snext, min(1, ngrp - 1));
     if (wlive) {
       a_load(a0, 0);
       if (nb > 1) a_load(a1, 1);
     }
-    b_store(0);
-    if (nb > 1) b_load(1);
+    b_store(breg0, 0);
+    if (nb > 1) b_store(breg1, 1);
+    if (nb > 2) b_load(breg0, 2);
 
     auto stage = [&](const v4i (&a)[4], int stg) {
       const int buf = stg & 1;
@@ -529,21 +534,24 @@ __global__ __launch_bounds__(256 * TG, 1) void k_tiled(
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) acc[rt][tt] = mfma_ij<0, 0>(a[rt], b.v, acc[rt][tt], sa[rt], sb);
           // keep the operand reads of one token tile next to its MFMAs
-          // (hoisting all eight tiles' reads would cost 64 registers)
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     };
+    // Stage stg reads LDS buffer stg & 1.  At its start (after the barrier)
+    // the rows of stage stg + 1 go from registers to the other buffer, whose
+    // readers (stage stg - 1) are past the barrier; the rows of stage stg + 3
+    // are requested into the register set just emptied.
     for (int stg = 0; stg < nb; stg += 2) {
-      __syncthreads();  // S.b[stg & 1] complete; readers of the other buffer are done
-      if (stg + 1 < nb) b_store(1);
-      if (stg + 2 < nb) b_load(stg + 2);
+      __syncthreads();
+      if (stg > 0 && stg + 1 < nb) b_store(breg1, 1);
+      if (stg + 3 < nb) b_load(breg1, stg + 3);
       stage(a0, stg);
       if (wlive && stg + 2 < nb) a_load(a0, stg + 2);
       if (stg + 1 < nb) {
         __syncthreads();
-        if (stg + 2 < nb) b_store(0);
-        if (stg + 3 < nb) b_load(stg + 3);
+        if (stg + 2 < nb) b_store(breg0, 0);
+        if (stg + 4 < nb) b_load(breg0, stg + 4);
         stage(a1, stg + 1);
         if (wlive && stg + 3 < nb) a_load(a1, stg + 3);
       }
@@ -556,22 +564,22 @@ __global__ __launch_bounds__(256 * TG, 1) void k_tiled(
 
     // ---- epilogue
     if (G1) {
-      float amx[8];
+      // SwiGLU in place: acc[0] / acc[1] become act of the gate tiles' columns
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[0][tt][r] = silu(acc[0][tt][r]) * acc[2][tt][r];
+          acc[1][tt][r] = silu(acc[1][tt][r]) * acc[3][tt][r];
+        }
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         float m = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          m = fmaxf(m, fabsf(silu(acc[0][tt][r]) * acc[2][tt][r]));
-          m = fmaxf(m, fabsf(silu(acc[1][tt][r]) * acc[3][tt][r]));
-        }
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fmaxf(fabsf(acc[0][tt][r]), fabsf(acc[1][tt][r])));
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
-        amx[tt] = m;
-      }
-      if (g == 0) {
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) S.amax[tg][wg][tt * 16 + l16] = amx[tt];
+        if (g == 0) S.amax[tg][wg][tt * 16 + l16] = m;
       }
       __syncthreads();
       const int nfb = F / kActBlock;
@@ -584,15 +592,11 @@ __global__ __launch_bounds__(256 * TG, 1) void k_tiled(
         const float am = fmaxf(fmaxf(S.amax[tg][0][tl], S.amax[tg][1][tl]),
                                fmaxf(S.amax[tg][2][tl], S.amax[tg][3][tl]));
         const int e = scale_exp(am);
-        float v[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = ldexpf(silu(acc[0][tt][r]) * acc[2][tt][r], -e);
-          v[4 + r] = ldexpf(silu(acc[1][tt][r]) * acc[3][tt][r], -e);
-        }
         uint8_t* ap = aq + (size_t)(r0 + tok) * F + f0 + 4 * g;
-        *reinterpret_cast<uint32_t*>(ap) = pack4_fp8(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<uint32_t*>(ap + 16) = pack4_fp8(v[4], v[5], v[6], v[7]);
+        *reinterpret_cast<uint32_t*>(ap) = pack4_fp8(ldexpf(acc[0][tt][0], -e), ldexpf(acc[0][tt][1], -e),
+                                                     ldexpf(acc[0][tt][2], -e), ldexpf(acc[0][tt][3], -e));
+        *reinterpret_cast<uint32_t*>(ap + 16) = pack4_fp8(ldexpf(acc[1][tt][0], -e), ldexpf(acc[1][tt][1], -e),
+                                                          ldexpf(acc[1][tt][2], -e), ldexpf(acc[1][tt][3], -e));
         if (wg == 0 && g == 0) as_[(size_t)(r0 + tok) * nfb + wb] = (uint8_t)(e + 127);
       }
     } else if (wlive) {

@@ -10,7 +10,7 @@ activation quantisation, GEMMs, SwiGLU, combine).
 from .inputs import (  # noqa: F401
     Dims,
     Workload,
-    CONFIGS,
+    WORKLOADS,
     dims_for,
     make,
     make_ep_shaped,

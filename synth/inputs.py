@@ -93,21 +93,23 @@ class Workload:
 
 
 # ----------------------------------------------------------------------------
-# The five workloads.  cfg ids 0..4:
-#   0 tiny: T=64, H=256, F=128, E=8, top-2, all experts local
-#   1 decode share: T=512, H=7168, F=2048, E=384, top-6, 48 local experts
-#   2 prefill share: T=8192, same shapes
-#   3 skewed routing + EPLB: T=8192, 448 physical slots (64 redundant), 56 local
-#   4 sweep: T in {1, 8, 64, 256, 512, 1024, 4096, 8192}, cfg-1 shapes
+# The named workloads ("key" seeds their draws):
+#   tiny: T=64, H=256, F=128, E=8, top-2, all experts local
+#   decode512: one EP8 rank's decode share, T=512, H=7168, F=2048, E=384,
+#              top-6, 48 local experts
+#   prefill8192: the prefill share, T=8192, same shapes
+#   eplb8192: skewed routing + EPLB, T=8192, 448 physical slots (64
+#             redundant), 56 local
+#   sweep: T in {1, 8, 64, 256, 512, 1024, 4096, 8192}, decode512 shapes
 # ----------------------------------------------------------------------------
 
-CONFIGS = {
-    0: dict(T=64, H=256, F=128, E=8, k=2, P_local=8, weights_key=0),
-    1: dict(T=512, H=7168, F=2048, E=384, k=6, P_local=48, weights_key=1),
-    2: dict(T=8192, H=7168, F=2048, E=384, k=6, P_local=48, weights_key=1),
-    3: dict(T=8192, H=7168, F=2048, E=384, k=6, P_local=56, weights_key=1,
-            redundant=64, ranks=8, zipf_s=1.2),
-    4: dict(T=None, H=7168, F=2048, E=384, k=6, P_local=48, weights_key=1),
+WORKLOADS = {
+    "tiny": dict(key=0, T=64, H=256, F=128, E=8, k=2, P_local=8, weights_key=0),
+    "decode512": dict(key=1, T=512, H=7168, F=2048, E=384, k=6, P_local=48, weights_key=1),
+    "prefill8192": dict(key=2, T=8192, H=7168, F=2048, E=384, k=6, P_local=48, weights_key=1),
+    "eplb8192": dict(key=3, T=8192, H=7168, F=2048, E=384, k=6, P_local=56, weights_key=1,
+                     redundant=64, ranks=8, zipf_s=1.2),
+    "sweep": dict(key=4, T=None, H=7168, F=2048, E=384, k=6, P_local=48, weights_key=1),
 }
 SWEEP_T = (1, 8, 64, 256, 512, 1024, 4096, 8192)
 
@@ -167,7 +169,7 @@ def _encode_mxfp4(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 # ----------------------------------------------------------------------------
-# Expert weights (cached per process: the 7168/2048 family is shared by cfg 1-4)
+# Expert weights (cached per process: the 7168/2048 family is shared by every full-size workload)
 # ----------------------------------------------------------------------------
 
 _W_CACHE: Dict[Tuple[int, int, int, int], Tuple[np.ndarray, ...]] = {}
@@ -231,7 +233,7 @@ def _tokens(key: int, sub: int, T: int, H: int, E: int, bias: Optional[np.ndarra
 
 
 # ----------------------------------------------------------------------------
-# Skewed routing (cfg 3): Zipf target popularity, closed-form bias, greedy map
+# Skewed routing (eplb8192): Zipf target popularity, closed-form bias, greedy map
 # ----------------------------------------------------------------------------
 
 def zipf_popularity(E: int, k: int, s: float, rng: np.random.Generator) -> np.ndarray:
@@ -320,11 +322,11 @@ def greedy_replica_map(p: np.ndarray, redundant: int, ranks: int):
 # Public constructors
 # ----------------------------------------------------------------------------
 
-def dims_for(cfg: int, T: Optional[int] = None, T_max: Optional[int] = None) -> Dims:
-    c = CONFIGS[cfg]
+def dims_for(name: str, T: Optional[int] = None, T_max: Optional[int] = None) -> Dims:
+    c = WORKLOADS[name]
     T = c["T"] if T is None else T
     E, k = c["E"], c["k"]
-    if cfg == 3:
+    if c.get("redundant"):
         P_total = E + c["redundant"]
         R_max = None  # fixed after the map is built
     else:
@@ -337,25 +339,27 @@ def _identity_map(E: int):
     return np.ones(E, np.int32), np.arange(E, dtype=np.int32)[:, None].copy()
 
 
-def make(cfg: int, T: Optional[int] = None, with_weights: bool = True,
+def make(name: str, T: Optional[int] = None, with_weights: bool = True,
          sub: int = 0, token_id_base: int = 0, p0: int = 0) -> Workload:
-    """Workload ``cfg`` (0..4).  ``T`` overrides the token count (required for 4).
+    """Workload ``name`` (a key of WORKLOADS).  ``T`` overrides the token count
+    (required for "sweep").
 
     ``sub`` selects an independent token draw (the virtual rank of the
     EP-shaped prefill case, or the T point of the sweep); ``p0`` moves this
     GPU's window of physical slots.
     """
-    c = CONFIGS[cfg]
-    if cfg == 4:
+    c = WORKLOADS[name]
+    key = c["key"]
+    if c["T"] is None:
         if T is None:
-            raise ValueError("cfg 4 needs T")
+            raise ValueError(f"workload {name} needs T")
         sub = T if sub == 0 else sub
-    d = dims_for(cfg, T)
+    d = dims_for(name, T)
     E, H, F, k = d.E, d.H, d.F, d.k
     bias = None
     pop = None
-    if cfg == 3:
-        g = _rng(cfg, STREAM_EPLB, 0)
+    if c.get("redundant"):
+        g = _rng(key, STREAM_EPLB, 0)
         pop = zipf_popularity(E, k, c["zipf_s"], g)
         bias = zipf_bias(pop, k)
         rep_count, rep_slots, all_slot_expert = greedy_replica_map(pop, c["redundant"], c["ranks"])
@@ -367,37 +371,37 @@ def make(cfg: int, T: Optional[int] = None, with_weights: bool = True,
     if p0 < 0 or p0 + d.P_local > d.P_total:
         raise ValueError("local slot window out of range")
     slot_expert = all_slot_expert[p0:p0 + d.P_local].copy()
-    logits, x = _tokens(cfg, sub, d.T, H, E, bias)
+    logits, x = _tokens(key, sub, d.T, H, E, bias)
     if with_weights:
         w1, w1s, w2, w2s = _slot_weights(c["weights_key"], H, F, slot_expert)
     else:
         z = np.zeros((0,), np.uint8)
         w1 = w1s = w2 = w2s = z
-    return Workload(name=f"cfg{cfg}" + (f"_T{d.T}" if cfg == 4 else ""), dims=d,
+    return Workload(name=name + (f"_T{d.T}" if c["T"] is None else ""), dims=d,
                     logits=logits, x=x, rep_count=rep_count, rep_slots=rep_slots,
                     slot_expert=slot_expert, w1=w1, w1s=w1s, w2=w2, w2s=w2s,
                     popularity=pop)
 
 
 def make_sweep(T: int, with_weights: bool = True) -> Workload:
-    return make(4, T=T, with_weights=with_weights)
+    return make("sweep", T=T, with_weights=with_weights)
 
 
 def make_ep_shaped(ranks: int = 8, T_rank: int = 8192, with_weights: bool = True) -> Workload:
     """The prefill share at a real EP rank's load.
 
     ``ranks`` virtual ranks of ``T_rank`` tokens each (rank r's tokens are the
-    cfg-2 draw with sub = r, global ids r*T_rank + t) all route into this
+    prefill8192 draw with sub = r, global ids r*T_rank + t) all route into this
     GPU's 48 experts, as every rank's tokens do under EP8.
     """
-    parts = [make(2, with_weights=False, sub=r) for r in range(ranks)]
+    parts = [make("prefill8192", with_weights=False, sub=r) for r in range(ranks)]
     base = parts[0]
     logits = np.concatenate([p.logits for p in parts])
     x = np.concatenate([p.x for p in parts])
     T = ranks * T_rank
     d = base.dims.replace(T=T, T_max=T)
-    w = make(2, T=1, with_weights=with_weights) if with_weights else base
-    return Workload(name=f"cfg2_ep{ranks}", dims=d, logits=logits, x=x,
+    w = make("prefill8192", T=1, with_weights=with_weights) if with_weights else base
+    return Workload(name=f"prefill8192_ep{ranks}", dims=d, logits=logits, x=x,
                     rep_count=base.rep_count, rep_slots=base.rep_slots,
                     slot_expert=base.slot_expert, w1=w.w1, w1s=w.w1s, w2=w.w2, w2s=w.w2s)
 

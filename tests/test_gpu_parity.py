@@ -46,7 +46,7 @@ def _full_check(wl, path="auto"):
 
 @pytest.mark.parametrize("path", ["auto", "small_m", "staged", "large_m"])
 def test_tiny_all_paths(path):
-    res = _full_check(synth.make(0), path)
+    res = _full_check(synth.make("tiny"), path)
     assert res["chosen"] == ("small_m" if path == "auto" else path)
 
 
@@ -192,17 +192,17 @@ def _big_check(wl, n_slots=3, n_tokens=24, path="auto"):
 
 
 def test_decode_share_512_tokens():
-    res = _big_check(synth.make(1))
+    res = _big_check(synth.make("decode512"))
     assert res["chosen"] == "small_m"
 
 
 def test_prefill_share_8192_tokens():
-    res = _big_check(synth.make(2))
+    res = _big_check(synth.make("prefill8192"))
     assert res["chosen"] == "large_m"
 
 
 def test_skewed_routing_with_eplb_8192_tokens():
-    wl = synth.make(3)
+    wl = synth.make("eplb8192")
     res = _big_check(wl)
     # the recorder saw every pair, on all 448 physical slots
     assert res["hist"].sum() == wl.dims.T * wl.dims.k and wl.dims.P_total == 448

@@ -36,7 +36,7 @@ def test_scale_exponent_is_the_smallest_power():
 
 
 def test_quant_blocks_matches_torch_cast():
-    wl = synth.make(0, with_weights=False)
+    wl = synth.make("tiny", with_weights=False)
     v = fm.bf16_to_f64(wl.x)
     q, s = om.quant_blocks(v)
     e = s.astype(np.int64) - 127
@@ -137,7 +137,7 @@ def test_identity_expert_hand_values():
 
 
 def test_zero_experts_give_zero_output():
-    wl = synth.make(0)
+    wl = synth.make("tiny")
     wl.rep_slots = wl.rep_slots + 100          # every pair lands outside this GPU's slots
     d = wl.dims.replace(P_total=200)
     wl.dims = d
@@ -150,7 +150,7 @@ def test_zero_experts_give_zero_output():
 
 def test_layer_second_formulation_per_token():
     """Bucketed O3-O9 equals the per-token sum over its experts, no permutation."""
-    wl = synth.make(0)
+    wl = synth.make("tiny")
     r = om.forward(wl)
     for t in range(wl.dims.T):
         o = om.forward_token(wl, t)
@@ -158,8 +158,8 @@ def test_layer_second_formulation_per_token():
         assert np.allclose(r["out"][t], o, rtol=0, atol=scale * 1e-12), t
 
 
-def test_layer_invariants_cfg0():
-    wl = synth.make(0)
+def test_layer_invariants_tiny():
+    wl = synth.make("tiny")
     d = wl.dims
     r = om.forward(wl)
     assert r["load_hist"].sum() == d.T * d.k
@@ -168,13 +168,13 @@ def test_layer_invariants_cfg0():
     assert r["out"].shape == (d.T, d.H) and np.all(np.isfinite(r["out"]))
 
 
-def test_rank_split_additivity_cfg0():
+def test_rank_split_additivity_tiny():
     """Two GPUs holding slots [0,4) and [4,8) produce partial sums that add to the full layer."""
-    wl = synth.make(0)
+    wl = synth.make("tiny")
     full = om.forward(wl)
     parts = []
     for p0 in (0, 4):
-        w = synth.make(0)
+        w = synth.make("tiny")
         d = w.dims.replace(P_local=4, p0=p0)
         w.dims = d
         w.w1, w.w1s, w.w2, w.w2s = (a[p0:p0 + 4] for a in (wl.w1, wl.w1s, wl.w2, wl.w2s))

@@ -210,7 +210,7 @@ def test_buckets_empty_and_all_remote():
 # ---------------------------------------------------------------- input tables
 
 def test_greedy_replica_map_is_a_valid_placement():
-    wl = synth.make(3, T=16, with_weights=False)
+    wl = synth.make("eplb8192", T=16, with_weights=False)
     d = wl.dims
     assert d.P_total == 448 and d.P_local == 56
     rc, rs = wl.rep_count, wl.rep_slots
@@ -226,7 +226,7 @@ def test_greedy_replica_map_is_a_valid_placement():
 
 
 def test_skewed_routing_is_skewed_and_map_balances_it():
-    wl = synth.make(3, T=2048, with_weights=False)
+    wl = synth.make("eplb8192", T=2048, with_weights=False)
     d = wl.dims
     ids, _ = om.route(wl.logits, d.k)
     share = np.bincount(ids.ravel(), minlength=d.E) / ids.size
