@@ -83,10 +83,14 @@ typedef enum {
 } moe_status_t;
 
 typedef enum {
-  MOE_PATH_AUTO = 0,    /* SMALL_M if T <= small_m_max, LARGE_M if T >= large_m_min, else STAGED */
-  MOE_PATH_SMALL_M = 1, /* weight-streaming kernels for a few rows per expert */
-  MOE_PATH_STAGED = 2,  /* the component calls in sequence */
-  MOE_PATH_LARGE_M = 3  /* tiled kernels for many rows per expert */
+  MOE_PATH_AUTO = 0,    /* SMALL_M if T <= min(small_m_max, 1024), LARGE_M if T >= large_m_min,
+                           else STAGED */
+  MOE_PATH_SMALL_M = 1, /* four launches in (token, j) pair order: route + remap + quant of every
+                           token; GEMM1 and GEMM2 weight streaming, each block listing its slot's
+                           pairs itself; combine + load record.  No bucket scan or permute.
+                           T <= 1024 (else MOE_ERR_UNSUPPORTED). */
+  MOE_PATH_STAGED = 2,  /* the component calls in sequence (bucketed rows, weight streaming) */
+  MOE_PATH_LARGE_M = 3  /* bucketed rows, persistent tiled GEMMs for many rows per expert */
 } moe_path_t;
 
 /* Problem sizes of one call.  Limits: 0 <= T <= T_max <= 1<<20; H, F
@@ -103,7 +107,13 @@ typedef struct {
 } moe_dims_t;
 
 /* Optional device copies of intermediate results for parity checks; any
- * member may be NULL.  Shapes as in the layout table above. */
+ * member may be NULL.  Shapes as in the layout table above.  Every path
+ * writes topk_ids, topk_w, phys_ids, counts and offsets.  STAGED and
+ * LARGE_M (bucketed rows) write row_of_pair, pair_of_row, xq, xs, aq, as;
+ * SMALL_M writes instead the per-token activations xq_tok u8 [T, H] /
+ * xs_tok u8 [T, H/128] (every token, local pairs or not) and the per-pair
+ * act rows aq_pair u8 [T*k, F] / as_pair u8 [T*k, F/128] (rows of local
+ * pairs only). */
 typedef struct {
   int32_t* topk_ids;
   float* topk_w;
@@ -116,6 +126,10 @@ typedef struct {
   uint8_t* xs;
   uint8_t* aq;
   uint8_t* as;
+  uint8_t* xq_tok;
+  uint8_t* xs_tok;
+  uint8_t* aq_pair;
+  uint8_t* as_pair;
 } moe_taps_t;
 
 /* Bytes of device workspace every call below needs for `dims` (sized by

@@ -55,7 +55,8 @@ class Dims(ctypes.Structure):
 class Taps(ctypes.Structure):
     """moe_taps_t"""
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_ids", "topk_w", "phys_ids", "counts", "offsets",
-                                                "row_of_pair", "pair_of_row", "xq", "xs", "aq", "as_")]
+                                                "row_of_pair", "pair_of_row", "xq", "xs", "aq", "as_",
+                                                "xq_tok", "xs_tok", "aq_pair", "as_pair")]
 
 
 _lib_handle = None
@@ -241,7 +242,8 @@ def make_taps(d: Dims, device="cuda") -> Dict[str, torch.Tensor]:
     return dict(topk_ids=z(TK, i32), topk_w=z(TK, f32), phys_ids=z(TK, i32), counts=z(d.P_local, i32),
                 offsets=z(d.P_local + 1, i32), row_of_pair=z(TK, i32), pair_of_row=z(TMK, i32),
                 xq=z(TMK * d.H, u8), xs=z(TMK * (d.H // 128), u8), aq=z(TMK * d.F, u8),
-                as_=z(TMK * (d.F // 128), u8))
+                as_=z(TMK * (d.F // 128), u8), xq_tok=z(d.T * d.H, u8), xs_tok=z(d.T * (d.H // 128), u8),
+                aq_pair=z(TK * d.F, u8), as_pair=z(TK * (d.F // 128), u8))
 
 
 def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, out, ws, load_hist=None,
@@ -254,7 +256,8 @@ def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, 
         need = dict(topk_ids=(i32, TK), topk_w=(f32, TK), phys_ids=(i32, TK), counts=(i32, d.P_local),
                     offsets=(i32, d.P_local + 1), row_of_pair=(i32, TK), pair_of_row=(i32, TMK),
                     xq=(u8, TMK * d.H), xs=(u8, TMK * (d.H // 128)), aq=(u8, TMK * d.F),
-                    as_=(u8, TMK * (d.F // 128)))
+                    as_=(u8, TMK * (d.F // 128)), xq_tok=(u8, d.T * d.H), xs_tok=(u8, d.T * (d.H // 128)),
+                    aq_pair=(u8, TK * d.F), as_pair=(u8, TK * (d.F // 128)))
         tp = Taps(**{n: _ptr(taps.get(n), n, *need[n]) for n in need})
     chosen = ctypes.c_int(-1)
     rc = lib().moe_forward(

@@ -17,84 +17,135 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// a1 route: one wavefront per token.  Lane l holds logits l, l+64, ...; each of
-// the k rounds takes a wave-wide argmax (largest logit, lower id on ties) over
-// the entries not yet taken.  Weights: sigmoid of the chosen logits divided by
-// their sum, in f32.
+// a1 route: one wavefront per token.  Lane l holds logits l, l + 64, ...; each
+// of the k rounds takes the wavefront's argmax (largest logit, lower id on
+// ties): a scan of the lane's own entries, a DPP reduction inside each 16-lane
+// row, and a scalar pick among the four row winners (read with readlane).
+// The winner's entry is then retired (set to -inf; inputs are finite).
+// Weights: sigmoid of the chosen logits over their sum, in f32 (lanes j < k
+// hold choice j, all in row 0, so the sum is the row's DPP tree).
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+constexpr int kRor8 = 0x128, kRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
+
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// (bv, bi) <- the better of itself and its DPP partner's.
+template <int CTRL>
+__device__ __forceinline__ void take_better(float& bv, int& bi) {
+  const float ov = dppf<CTRL>(bv);
+  const int oi = dpp<CTRL>(bi);
+  const bool take = better(ov, oi, bv, bi);
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float add_partner(float v) {
+  return v + dppf<CTRL>(v);
+}
+
+// Route one token per wavefront (`row`: its logits).  Lane j < k returns
+// choice j and its weight.
+template <int EPL>
+__device__ __forceinline__ void route64(const float* __restrict__ row, int E, int k, int lane, int& my_id,
+                                        float& my_w) {
+  float v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+  }
+  my_id = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) {
+      const bool t = v[i] > bv;  // ascending ids: strict > keeps the lower id
+      bv = t ? v[i] : bv;
+      bi = t ? lane + 64 * i : bi;
+    }
+    take_better<kRor8>(bv, bi);
+    take_better<kRor4>(bv, bi);
+    take_better<kQuadSwap2>(bv, bi);
+    take_better<kQuadSwap1>(bv, bi);
+    float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int si = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+      const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+      const int ri = __builtin_amdgcn_readlane(bi, 16 * r);
+      if (better(rv, ri, sv, si)) {
+        sv = rv;
+        si = ri;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = (lane + 64 * i == si) ? -INFINITY : v[i];
+    if (lane == j) {
+      my_id = si;
+      my_l = sv;
+    }
+  }
+  const float s = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.0f;
+  float sum = add_partner<kRor8>(s);
+  sum = add_partner<kRor4>(sum);
+  sum = add_partner<kQuadSwap2>(sum);
+  sum = add_partner<kQuadSwap1>(sum);
+  sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 0));
+  my_w = s / sum;
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
                                                int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // wave-uniform
-  const float* row = logits + (size_t)t * E;
-  float v[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : 0.0f;
-  }
-  uint32_t taken = 0;
-  int my_id = 0;
-  float my_l = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      int e = lane + 64 * i;
-      bool ok = e < E && !((taken >> i) & 1u);
-      if (ok && (bi == INT_MAX || v[i] > bv)) {  // ascending e: strict > keeps the lower id
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oi = __shfl_xor(bi, off);
-      bool take = (oi != INT_MAX) && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi));
-      if (take) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      my_id = bi;
-      my_l = bv;
-    }
-  }
-  float s = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.0f;
-  float sum = s;
-#pragma unroll
-  for (int off = 1; off <= 32; off <<= 1) sum += __shfl_xor(sum, off);
+  int id;
+  float wt;
+  route64<EPL>(logits + (size_t)t * E, E, k, lane, id, wt);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = s / sum;
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
   }
 }
 
-template <int EPL>
-static hipError_t route_epl(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st) {
-  k_route<EPL><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, ids, w);
-  return hipGetLastError();
+// Logits per lane, rounded up to an instantiated size (E <= 1024).
+static int route_epl(int E) {
+  const int e = (E + 63) / 64;
+  if (e <= 1) return 1;
+  if (e <= 2) return 2;
+  if (e <= 4) return 4;
+  if (e <= 6) return 6;
+  if (e <= 8) return 8;
+  if (e <= 12) return 12;
+  return 16;
 }
+
+#define MOE_ROUTE_CASES(X) X(1) X(2) X(4) X(6) X(8) X(12) X(16)
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  int epl = (E + 63) / 64;
-  switch (epl) {
-    case 1: return route_epl<1>(logits, T, E, k, ids, w, st);
-    case 2: return route_epl<2>(logits, T, E, k, ids, w, st);
-    case 3: return route_epl<3>(logits, T, E, k, ids, w, st);
-    case 4: return route_epl<4>(logits, T, E, k, ids, w, st);
-    case 5: case 6: return route_epl<6>(logits, T, E, k, ids, w, st);
-    case 7: case 8: return route_epl<8>(logits, T, E, k, ids, w, st);
-    case 9: case 10: case 11: case 12: return route_epl<12>(logits, T, E, k, ids, w, st);
-    default: return route_epl<16>(logits, T, E, k, ids, w, st);
+  const unsigned nb = (unsigned)((T + 3) / 4);
+  switch (route_epl(E)) {
+#define X(N) \
+  case N: k_route<N><<<nb, 256, 0, st>>>(logits, T, E, k, ids, w); break;
+    MOE_ROUTE_CASES(X)
+#undef X
   }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -245,6 +296,34 @@ hipError_t launch_scan(int nch, int P_total, int p0, int P_local, const int32_t*
   return hipGetLastError();
 }
 
+// a4 arithmetic for one lane's 8 columns of a 128-column block (16 lanes per
+// block): e = smallest integer with amax <= 448 * 2^e over the block, codes
+// RNE e4m3fn(x * 2^-e).  `ok` false: the lane holds zeros (columns past H).
+__device__ __forceinline__ int quant8(const uint16_t* __restrict__ src, bool ok, uint2& q) {
+  float v[8];
+  if (ok) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(src);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(wd[i] << 16);
+      v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+  const int e = scale_exp(am);
+  q.x = pack4_fp8(ldexpf(v[0], -e), ldexpf(v[1], -e), ldexpf(v[2], -e), ldexpf(v[3], -e));
+  q.y = pack4_fp8(ldexpf(v[4], -e), ldexpf(v[5], -e), ldexpf(v[6], -e), ldexpf(v[7], -e));
+  return e;
+}
+
 // ---------------------------------------------------------------------------
 // a3 (part 3) + a4: one wavefront per (token, 512-column chunk).  Lanes j < k
 // resolve the row of pair (t, j) (base of its chunk and slot + rank; the
@@ -287,28 +366,8 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
   const int b = ch * 4 + (lane >> 4);
   const bool ok = b < nb;
   const int sub = lane & 15;  // 8 columns each
-  float v[8];
-  if (ok) {
-    uint4 raw = *reinterpret_cast<const uint4*>(x + (size_t)t * H + b * kActBlock + sub * 8);
-    uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(wd[i] << 16);
-      v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  float am = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
-  const int e = scale_exp(am);
   uint2 q;
-  q.x = pack4_fp8(ldexpf(v[0], -e), ldexpf(v[1], -e), ldexpf(v[2], -e), ldexpf(v[3], -e));
-  q.y = pack4_fp8(ldexpf(v[4], -e), ldexpf(v[5], -e), ldexpf(v[6], -e), ldexpf(v[7], -e));
+  const int e = quant8(x + (size_t)t * H + b * kActBlock + sub * 8, ok, q);
   if (ok) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -391,6 +450,210 @@ hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* ro
   if (T == 0) return hipSuccess;
   const long waves = (long)T * ((H + 511) / 512);
   k_combine<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, y, row_of_pair, w, out);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// Small-M path front and back ends.  The small-input path keeps (token, j)
+// pair order instead of bucket rows: the GEMM blocks list their slot's pairs
+// themselves, so no scan or permute runs between routing and GEMM1.
+// ===========================================================================
+
+// a1 + a2 + a4 in one launch.  Blocks [0, nr) route 16 tokens each (one per
+// wavefront), remap them and count the chunk's pairs per physical slot into
+// partial[chunk][P_total]; the replica tables are staged in LDS while the
+// logits load when they fit.  Blocks [nr, ...) quantise every token (one
+// wavefront per token and 512 columns) into per-token rows xq_tok / xs_tok.
+constexpr int kFrontThreads = 1024;
+constexpr int kRepLds = 4096;  // replica-table entries staged in LDS
+
+template <int EPL>
+__global__ __launch_bounds__(kFrontThreads) void k_front(
+    int T, int E, int k, int H, const float* __restrict__ logits, const uint16_t* __restrict__ x,
+    const int32_t* __restrict__ rep_count, const int32_t* __restrict__ rep_slots, int R_max,
+    uint32_t token_id_base, int P_total, int nr, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ phys, int32_t* __restrict__ partial, uint8_t* __restrict__ xq_tok,
+    uint8_t* __restrict__ xs_tok) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < nr) {
+    __shared__ int s_rc[1024];
+    __shared__ int s_rs[kRepLds];
+    __shared__ int s_phys[16 * 16];
+    const bool lds_tab = E * R_max <= kRepLds;
+    for (int i = threadIdx.x; i < E; i += kFrontThreads) s_rc[i] = rep_count[i];
+    if (lds_tab)
+      for (int i = threadIdx.x; i < E * R_max; i += kFrontThreads) s_rs[i] = rep_slots[i];
+    const int t = blockIdx.x * 16 + wave;
+    const bool tv = t < T;  // wave-uniform
+    int id = 0;
+    float wt = 0.0f;
+    if (tv) route64<EPL>(logits + (size_t)t * E, E, k, lane, id, wt);
+    __syncthreads();  // replica tables staged
+    int p = -1;       // never matches a slot
+    if (tv && lane < k) {
+      const size_t pr = (size_t)t * k + lane;
+      const uint32_t h = fmix32(token_id_base + (uint32_t)t);
+      const int r = (int)(h % (uint32_t)s_rc[id]);
+      p = lds_tab ? s_rs[id * R_max + r] : rep_slots[(size_t)id * R_max + r];
+      ids[pr] = id;
+      w[pr] = wt;
+      phys[pr] = p;
+    }
+    if (lane < k) s_phys[wave * k + lane] = p;
+    __syncthreads();
+    const int np = 16 * k;
+    for (int q = threadIdx.x; q < P_total; q += kFrontThreads) {
+      int cnt = 0;
+      for (int i = 0; i < np; ++i) cnt += s_phys[i] == q;  // same address in every lane: a broadcast
+      partial[(size_t)blockIdx.x * P_total + q] = cnt;
+    }
+    return;
+  }
+  const int nb = H / kActBlock;
+  const int nc = (nb + 3) / 4;
+  const int wid = ((int)blockIdx.x - nr) * 16 + wave;
+  const int t = wid / nc, ch = wid - t * nc;
+  if (t >= T) return;  // wave-uniform
+  const int b = ch * 4 + (lane >> 4);
+  const bool ok = b < nb;
+  const int sub = lane & 15;
+  uint2 q;
+  const int e = quant8(x + (size_t)t * H + b * kActBlock + sub * 8, ok, q);
+  if (ok) {
+    *reinterpret_cast<uint2*>(xq_tok + (size_t)t * H + b * kActBlock + sub * 8) = q;
+    if (sub == 0) xs_tok[(size_t)t * nb + b] = (uint8_t)(e + 127);
+  }
+}
+
+hipError_t launch_front(int T, int E, int k, int H, const float* logits, const uint16_t* x, const int32_t* rep_count,
+                        const int32_t* rep_slots, int R_max, uint32_t token_id_base, int P_total, int32_t* ids,
+                        float* w, int32_t* phys, int32_t* partial, uint8_t* xq_tok, uint8_t* xs_tok,
+                        hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const int nr = (T + 15) / 16;
+  const long waves = (long)T * ((H / kActBlock + 3) / 4);
+  const unsigned grid = (unsigned)(nr + (waves + 15) / 16);
+  switch (route_epl(E)) {
+#define X(N)                                                                                                   \
+  case N:                                                                                                      \
+    k_front<N><<<grid, kFrontThreads, 0, st>>>(T, E, k, H, logits, x, rep_count, rep_slots, R_max,             \
+                                               token_id_base, P_total, nr, ids, w, phys, partial, xq_tok,     \
+                                               xs_tok);                                                       \
+    break;
+    MOE_ROUTE_CASES(X)
+#undef X
+  }
+  return hipGetLastError();
+}
+
+// a7 over pair-indexed GEMM2 rows: out[t] = bf16_rne(sum over local j,
+// ascending, of w[t][j] * y[t * k + j]) (the same f32 fma chain as
+// k_combine).  Extra blocks after the ncomb combine blocks finish the load
+// record: nred blocks add the routing blocks' chunk counts into load_hist
+// (64 slots per block, four chunk groups per slot reduced in LDS), and the
+// last block turns the per-slot counts (written by GEMM1) into offsets.
+__global__ __launch_bounds__(256) void k_combine_pairs(int T, int H, int k, const float* __restrict__ y,
+                                                       const int32_t* __restrict__ phys, int p0, int P_local,
+                                                       const float* __restrict__ w, uint16_t* __restrict__ out,
+                                                       int ncomb, int nred, const int32_t* __restrict__ partial,
+                                                       int nch, int P_total, int32_t* __restrict__ load_hist,
+                                                       const int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets) {
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= ncomb) {
+    const int r = (int)blockIdx.x - ncomb;
+    if (r < nred) {
+      __shared__ int s_red[4][64];
+      const int ql = tid & 63, cg = tid >> 6;
+      const int q = 64 * r + ql;
+      int sum = 0;
+      if (q < P_total)
+        for (int c = cg; c < nch; c += 4) sum += partial[(size_t)c * P_total + q];
+      s_red[cg][ql] = sum;
+      __syncthreads();
+      if (cg == 0 && q < P_total) load_hist[q] += (s_red[0][ql] + s_red[1][ql]) + (s_red[2][ql] + s_red[3][ql]);
+      return;
+    }
+    // offsets: thread i scans slots [4i, 4i + 4), then a Hillis-Steele scan of the 256 partial sums
+    __shared__ int s_scan[256];
+    int loc[4], run = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sl = 4 * tid + u;
+      loc[u] = run;
+      run += sl < P_local ? counts[sl] : 0;
+    }
+    s_scan[tid] = run;
+    for (int off = 1; off < 256; off <<= 1) {
+      __syncthreads();
+      const int o = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += o;
+    }
+    __syncthreads();
+    const int before = tid > 0 ? s_scan[tid - 1] : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sl = 4 * tid + u;
+      if (sl < P_local) offsets[sl] = before + loc[u];
+    }
+    if (tid == blockDim.x - 1) offsets[P_local] = s_scan[tid];
+    return;
+  }
+  const int lane = tid & 63;
+  const int nc = (H + 511) / 512;
+  const int wid = blockIdx.x * 4 + (tid >> 6);
+  const int t = wid / nc, ch = wid - t * nc;
+  if (t >= T) return;
+  int mine = 0;
+  float myw = 0.0f;
+  if (lane < k) {
+    const int p = phys[(size_t)t * k + lane];
+    mine = p >= p0 && p < p0 + P_local;
+    myw = w[(size_t)t * k + lane];
+  }
+  const uint64_t local = __ballot(mine);
+  float ws[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ws[j] = __shfl(myw, j);
+  const int h = ch * 512 + lane * 8;
+  if (h >= H) return;
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float wj = ws[j];
+    if (j >= k || !((local >> j) & 1u)) continue;  // wave-uniform
+    const float* yr = y + ((size_t)t * k + j) * H + h;
+    const float4 y0 = *reinterpret_cast<const float4*>(yr);
+    const float4 y1 = *reinterpret_cast<const float4*>(yr + 4);
+    a[0] = fmaf(wj, y0.x, a[0]);
+    a[1] = fmaf(wj, y0.y, a[1]);
+    a[2] = fmaf(wj, y0.z, a[2]);
+    a[3] = fmaf(wj, y0.w, a[3]);
+    a[4] = fmaf(wj, y1.x, a[4]);
+    a[5] = fmaf(wj, y1.y, a[5]);
+    a[6] = fmaf(wj, y1.z, a[6]);
+    a[7] = fmaf(wj, y1.w, a[7]);
+  }
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(a[4]) | ((uint32_t)f32_to_bf16(a[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(a[6]) | ((uint32_t)f32_to_bf16(a[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * H + h) = o;
+}
+
+hipError_t launch_combine_pairs(int T, int H, int k, const float* y, const int32_t* phys, int p0, int P_local,
+                                const float* w, uint16_t* out, const int32_t* partial, int nch, int P_total,
+                                int32_t* load_hist, const int32_t* counts, int32_t* offsets, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const long waves = (long)T * ((H + 511) / 512);
+  const int ncomb = (int)((waves + 3) / 4);
+  const int nred = load_hist ? (P_total + 63) / 64 : 0;
+  k_combine_pairs<<<(unsigned)(ncomb + nred + 1), 256, 0, st>>>(T, H, k, y, phys, p0, P_local, w, out, ncomb, nred,
+                                                                partial, nch, P_total, load_hist, counts, offsets);
   return hipGetLastError();
 }
 

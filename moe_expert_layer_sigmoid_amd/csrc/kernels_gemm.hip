@@ -183,37 +183,151 @@ __device__ __forceinline__ void stream_tile(v4f (&acc)[4], const SOps& O, int S4
   }
 }
 
-// Stage the token tile's 128-column scales in LDS: rows of 2 * S4 bytes,
-// zero beyond K/128 (padded steps).
-__device__ __forceinline__ void stage_token_scales(uint8_t* s_xs, const uint8_t* xs, int nrow, int nb, int S4) {
+constexpr int kMaxSteps = 64;    // K <= 16384
+constexpr int kPairRows = kPairMaxT;  // rows of one slot on the pair-indexed path
+
+// The pairs (t, j) whose physical slot is q, ascending, into list[0, cap);
+// returns their number (the same in every thread).  256 threads; each
+// iteration covers 1024 pairs, four consecutive ones per thread, placed by
+// ballots within a wavefront and by the wavefront totals across the block.
+__device__ __forceinline__ int4 pairs4(const int32_t* __restrict__ phys, int np, int i0) {
+  if (i0 + 3 < np) return *reinterpret_cast<const int4*>(phys + i0);
+  int4 v;
+  v.x = i0 < np ? phys[i0] : -1;
+  v.y = i0 + 1 < np ? phys[i0 + 1] : -1;
+  v.z = i0 + 2 < np ? phys[i0 + 2] : -1;
+  v.w = i0 + 3 < np ? phys[i0 + 3] : -1;
+  return v;
+}
+
+__device__ int slot_pairs(const int32_t* __restrict__ phys, int np, int q, int* list, int cap, int (*s_cnt)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int run = 0, buf = 0;
+  int4 cur = pairs4(phys, np, 4 * tid);
+  for (int base = 0; base < np; base += 1024) {
+    const int i0 = base + 4 * tid;
+    const int4 nxt = base + 1024 < np ? pairs4(phys, np, i0 + 1024) : int4{-1, -1, -1, -1};  // one ahead
+    const int v[4] = {cur.x, cur.y, cur.z, cur.w};
+    int before = 0, total = 0;
+    bool f[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f[m] = v[m] == q;
+      const uint64_t bal = __ballot(f[m]);
+      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      total += __popcll(bal);
+    }
+    if (lane == 0) s_cnt[buf][wave] = total;
+    __syncthreads();
+    int pos = run + before, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int cw = s_cnt[buf][w];
+      pos += w < wave ? cw : 0;
+      all += cw;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (f[m]) {
+        if (pos < cap) list[pos] = i0 + m;
+        ++pos;
+      }
+    run += all;
+    buf ^= 1;
+    cur = nxt;
+  }
+  __syncthreads();  // the list is complete
+  return run;
+}
+
+// Stage a token tile's 128-column scales in LDS: 16 rows of 2 * S4 bytes,
+// zero beyond K/128 (padded steps) and beyond the tile's rows.
+template <typename Src>
+__device__ __forceinline__ void stage_token_scales(uint8_t* s_xs, const uint8_t* xs, int nrow, int nb, int S4,
+                                                   Src src) {
   const int pitch = 2 * S4;
   for (int i = threadIdx.x; i < 16 * pitch; i += blockDim.x) {
     const int r = i / pitch, c = i - r * pitch;
-    s_xs[i] = (r < nrow && c < nb) ? xs[(size_t)r * nb + c] : (uint8_t)0;
+    s_xs[i] = (r < nrow && c < nb) ? xs[(size_t)src(r) * nb + c] : (uint8_t)0;
   }
 }
 
-constexpr int kMaxSteps = 64;  // K <= 16384
+// Rows of one slot for the streaming GEMMs.  Bucketed: the slot's rows are
+// [offsets[s], offsets[s+1]) of the per-row buffers (input and output share
+// the index).  Pair-indexed: the slot's pairs p (ascending), input row
+// p / div (div = k for GEMM1's per-token activations, 1 for GEMM2), output
+// row p.
+template <bool PAIRS>
+struct SlotRows {
+  int n, row0, div;
+  const int* list;
+  __device__ int src(int r) const { return PAIRS ? list[r] / div : row0 + r; }
+  __device__ int dst(int r) const { return PAIRS ? list[r] : row0 + r; }
+};
+
+template <bool PAIRS>
+__device__ __forceinline__ SlotRows<PAIRS> slot_rows(const int32_t* offsets, const int32_t* phys, int np, int q,
+                                                     int s, int div, int* list, int (*s_cnt)[4]) {
+  SlotRows<PAIRS> R;
+  R.div = div;
+  R.list = list;
+  if (PAIRS) {
+    R.row0 = 0;
+    R.n = min(slot_pairs(phys, np, q, list, kPairRows, s_cnt), kPairRows);
+  } else {
+    R.row0 = offsets[s];
+    R.n = offsets[s + 1] - R.row0;
+  }
+  return R;
+}
+
+// The token operand of one 16-row tile: a buffer over the input rows and
+// this lane's byte offsets.  Lanes past the tile's rows read zeros (pair-
+// indexed: an offset past the buffer) or row 0 of the tile (bucketed); their
+// results are never stored.
+template <bool PAIRS>
+__device__ __forceinline__ void token_operand(SOps& O, const uint8_t* x, const SlotRows<PAIRS>& R, int tt0, int nrow,
+                                              int nsrc, int K, int l16, int g) {
+  const bool tv = l16 < nrow;
+  if (PAIRS) {
+    const uint32_t lim = (uint32_t)nsrc * (uint32_t)K;
+    O.x = make_rsrc(x, lim);
+    O.xlo = tv ? (uint32_t)R.src(tt0 + l16) * (uint32_t)K + (uint32_t)g * 16 : lim;
+  } else {
+    O.x = make_rsrc(x + (size_t)(R.row0 + tt0) * K, (uint32_t)nrow * K);
+    O.xlo = (tv ? (uint32_t)l16 : 0u) * (uint32_t)K + (uint32_t)g * 16;
+  }
+  O.xhi = O.xlo + 64;
+}
 
 // ---------------------------------------------------------------------------
 // a5: one block per (local slot s, 128-column block fb of F).  Wave w owns the
 // gate tiles of columns fb*128 + 32w + [0, 32) and the matching up tiles, so
 // SwiGLU pairs registers of the same lane; the requant amax over the 128
 // columns is reduced across the four waves in LDS.
+//   bucketed (PAIRS false): xq/xs rows and aq/as rows from `offsets`;
+//   pair-indexed (PAIRS true): xq/xs are per-token rows [nsrc = T], aq/as
+//   per-pair rows [T*k]; the slot's pairs come from phys[0, np).
 // ---------------------------------------------------------------------------
+template <bool PAIRS>
 __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restrict__ xq,
                                                          const uint8_t* __restrict__ xs,
                                                          const int32_t* __restrict__ offsets,
-                                                         const uint8_t* __restrict__ pw1,
+                                                         const int32_t* __restrict__ phys, int np, int k, int p0,
+                                                         int nsrc, const uint8_t* __restrict__ pw1,
                                                          const uint8_t* __restrict__ pw1s, uint8_t* __restrict__ aq,
-                                                         uint8_t* __restrict__ as_, int H, int F) {
+                                                         uint8_t* __restrict__ as_, int32_t* __restrict__ counts,
+                                                         int H, int F) {
   __shared__ float s_amax[4][16];
   __shared__ __align__(16) uint8_t s_xs[16 * 2 * kMaxSteps];
+  __shared__ int s_list[PAIRS ? kPairRows : 1];
+  __shared__ int s_cnt[2][4];
   const int nfb = F / kActBlock;
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nfb, fb = item - s * nfb;
-  const int row0 = offsets[s];
-  const int n = offsets[s + 1] - row0;
+  const SlotRows<PAIRS> R = slot_rows<PAIRS>(offsets, phys, np, p0 + s, s, k, s_list, s_cnt);
+  const int n = R.n;
+  if (PAIRS && fb == 0 && threadIdx.x == 0) counts[s] = n;
   if (n <= 0) return;  // block-uniform: an idle expert reads no weights
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -235,13 +349,10 @@ __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restri
     const bool tv = tok < n;
     const int nrow = min(16, n - tt0);
     __syncthreads();  // previous tile's readers of s_xs / s_amax are done
-    stage_token_scales(s_xs, xs + (size_t)(row0 + tt0) * nb, nrow, nb, S4);
+    stage_token_scales(s_xs, xs, nrow, nb, S4, [&](int r) { return R.src(tt0 + r); });
     __syncthreads();
-    const uint32_t tr = tv ? (uint32_t)l16 : 0u;
-    O.x = make_rsrc(xq + (size_t)(row0 + tt0) * H, (uint32_t)nrow * H);
-    O.xlo = tr * (uint32_t)H + (uint32_t)g * 16;
-    O.xhi = O.xlo + 64;
-    O.sxs = s_xs + tr * 2 * S4;
+    token_operand<PAIRS>(O, xq, R, tt0, nrow, nsrc, H, l16, g);
+    O.sxs = s_xs + (tv ? l16 : 0) * 2 * S4;
     v4f acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -263,32 +374,38 @@ __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restri
     am = fmaxf(fmaxf(s_amax[0][l16], s_amax[1][l16]), fmaxf(s_amax[2][l16], s_amax[3][l16]));
     const int e = scale_exp(am);
     if (tv) {
-      uint8_t* ap = aq + (size_t)(row0 + tok) * F + f0 + 4 * g;
+      const size_t d = (size_t)R.dst(tok);
+      uint8_t* ap = aq + d * F + f0 + 4 * g;
       *reinterpret_cast<uint32_t*>(ap) =
           pack4_fp8(ldexpf(act[0], -e), ldexpf(act[1], -e), ldexpf(act[2], -e), ldexpf(act[3], -e));
       *reinterpret_cast<uint32_t*>(ap + 16) =
           pack4_fp8(ldexpf(act[4], -e), ldexpf(act[5], -e), ldexpf(act[6], -e), ldexpf(act[7], -e));
-      if (wave == 0 && g == 0) as_[(size_t)(row0 + tok) * nfb + fb] = (uint8_t)(e + 127);
+      if (wave == 0 && g == 0) as_[d * nfb + fb] = (uint8_t)(e + 127);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // a6: one block per (local slot s, 256-row block of H).  Wave w owns rows
-// hb*256 + 64w + [0, 64) as four 16-row tiles; y rows are f32 [rows, H].
+// hb*256 + 64w + [0, 64) as four 16-row tiles; y rows are f32 [rows, H]
+// (bucketed rows, or pair rows with the act rows pair-indexed too).
 // ---------------------------------------------------------------------------
+template <bool PAIRS>
 __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restrict__ aq,
                                                          const uint8_t* __restrict__ as_,
                                                          const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ phys, int np, int p0, int nsrc,
                                                          const uint8_t* __restrict__ pw2,
                                                          const uint8_t* __restrict__ pw2s, float* __restrict__ y,
                                                          int H, int F) {
   __shared__ __align__(16) uint8_t s_xs[16 * 2 * kMaxSteps];
+  __shared__ int s_list[PAIRS ? kPairRows : 1];
+  __shared__ int s_cnt[2][4];
   const int nhb = (H + 255) / 256;
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nhb, hb = item - s * nhb;
-  const int row0 = offsets[s];
-  const int n = offsets[s + 1] - row0;
+  const SlotRows<PAIRS> R = slot_rows<PAIRS>(offsets, phys, np, p0 + s, s, 1, s_list, s_cnt);
+  const int n = R.n;
   if (n <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -311,20 +428,17 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
     const bool tv = tok < n;
     const int nrow = min(16, n - tt0);
     __syncthreads();
-    stage_token_scales(s_xs, as_ + (size_t)(row0 + tt0) * nb, nrow, nb, S4);
+    stage_token_scales(s_xs, as_, nrow, nb, S4, [&](int r) { return R.src(tt0 + r); });
     __syncthreads();
     if (!live) continue;
-    const uint32_t tr = tv ? (uint32_t)l16 : 0u;
-    O.x = make_rsrc(aq + (size_t)(row0 + tt0) * F, (uint32_t)nrow * F);
-    O.xlo = tr * (uint32_t)F + (uint32_t)g * 16;
-    O.xhi = O.xlo + 64;
-    O.sxs = s_xs + tr * 2 * S4;
+    token_operand<PAIRS>(O, aq, R, tt0, nrow, nsrc, F, l16, g);
+    O.sxs = s_xs + (tv ? l16 : 0) * 2 * S4;
     v4f acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
     stream_tile(acc, O, S4);
     if (tv) {
-      float* yr = y + (size_t)(row0 + tok) * H + h0 + 4 * g;
+      float* yr = y + (size_t)R.dst(tok) * H + h0 + 4 * g;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
         *reinterpret_cast<float4*>(yr + 16 * rt) = make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]);
@@ -335,19 +449,33 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
 hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
                                const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
                                hipStream_t st) {
-  k_gemm1_stream<<<P_local * (F / kActBlock), 256, 0, st>>>(xq, xs, offsets, pw1, pw1s, aq, as, H, F);
+  k_gemm1_stream<false><<<P_local * (F / kActBlock), 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s,
+                                                                   aq, as, nullptr, H, F);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                                const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
-  k_gemm2_stream<<<P_local * ((H + 255) / 256), 256, 0, st>>>(aq, as, offsets, pw2, pw2s, y, H, F);
+  k_gemm2_stream<false><<<P_local * ((H + 255) / 256), 256, 0, st>>>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y,
+                                                                     H, F);
   return hipGetLastError();
 }
 
-}  // namespace moe
+hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, const int32_t* phys, int T, int k, int p0,
+                              const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int32_t* counts,
+                              int H, int F, int P_local, hipStream_t st) {
+  k_gemm1_stream<true><<<P_local * (F / kActBlock), 256, 0, st>>>(xq_tok, xs_tok, nullptr, phys, T * k, k, p0, T,
+                                                                  pw1, pw1s, aq, as, counts, H, F);
+  return hipGetLastError();
+}
 
-namespace moe {
+hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
+                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local,
+                              hipStream_t st) {
+  k_gemm2_stream<true><<<P_local * ((H + 255) / 256), 256, 0, st>>>(aq, as, nullptr, phys, T * k, p0, T * k, pw2,
+                                                                    pw2s, y, H, F);
+  return hipGetLastError();
+}
 
 // ===========================================================================
 // Large-M path: persistent tiled kernel.

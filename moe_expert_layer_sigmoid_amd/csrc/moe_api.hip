@@ -35,7 +35,9 @@ Layout layout_of(const moe_dims_t* d) {
   L.w = take(TK * 4);
   L.phys = take(TK * 4);
   L.rank = take(TK * 4);
-  L.partial = take(nch * d->P_total * 4);
+  // chunk counts: 64-token chunks (staged and large-M), 16-token chunks (small-M)
+  const size_t nch16 = ((size_t)(d->T_max < kPairMaxT ? d->T_max : kPairMaxT) + kFrontTokens - 1) / kFrontTokens;
+  L.partial = take((nch > nch16 ? nch : nch16) * d->P_total * 4);
   L.base = take(nch * d->P_local * 4);
   L.counts = take((size_t)d->P_local * 4);
   L.offsets = take(((size_t)d->P_local + 1) * 4);
@@ -123,7 +125,7 @@ moe_path_t moe_select_path(const moe_dims_t* d) {
   if (!d) return MOE_PATH_AUTO;
   const int small = d->small_m_max > 0 ? d->small_m_max : 512;
   const int large = d->large_m_min > 0 ? d->large_m_min : 1024;
-  if (d->T <= small) return MOE_PATH_SMALL_M;
+  if (d->T <= small && d->T <= kPairMaxT) return MOE_PATH_SMALL_M;
   if (d->T >= large) return MOE_PATH_LARGE_M;
   return MOE_PATH_STAGED;
 }
@@ -256,13 +258,15 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
       !dev_ok(rep_count) || !dev_ok(rep_slots) || !opt_ok(load_hist) || !dev_ok(out))
     return MOE_ERR_INVALID_ARG;
   if (taps) {
-    const void* tp[] = {taps->topk_ids, taps->topk_w, taps->phys_ids, taps->counts, taps->offsets, taps->row_of_pair,
-                        taps->pair_of_row, taps->xq, taps->xs, taps->aq, taps->as};
+    const void* tp[] = {taps->topk_ids, taps->topk_w,  taps->phys_ids, taps->counts,  taps->offsets,
+                        taps->row_of_pair, taps->pair_of_row, taps->xq, taps->xs, taps->aq,
+                        taps->as, taps->xq_tok, taps->xs_tok, taps->aq_pair, taps->as_pair};
     for (const void* p : tp)
       if (!opt_ok(p)) return MOE_ERR_INVALID_ARG;
   }
   if ((rc = check_ws(d, ws, ws_bytes))) return rc;
   const moe_path_t p = path == MOE_PATH_AUTO ? moe_select_path(d) : path;
+  if (p == MOE_PATH_SMALL_M && d->T > kPairMaxT) return MOE_ERR_UNSUPPORTED;
   if (chosen) *chosen = p;
   if (d->T == 0) return MOE_OK;
 
@@ -288,6 +292,23 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
   int32_t* partial = at<int32_t>(ws, L.partial);
   int32_t* base = at<int32_t>(ws, L.base);
   float* y = at<float>(ws, L.y);
+
+  if (p == MOE_PATH_SMALL_M) {
+    // pair-indexed: per-token activations in the xq/xs regions, pair rows in aq/as/y
+    uint8_t* xq_tok = pick(tp.xq_tok, L.xq);
+    uint8_t* xs_tok = pick(tp.xs_tok, L.xs);
+    uint8_t* aq_p = pick(tp.aq_pair, L.aq);
+    uint8_t* as_p = pick(tp.as_pair, L.as);
+    MOE_TRY(launch_front(d->T, d->E, d->k, d->H, logits, x, rep_count, rep_slots, d->R_max, d->token_id_base,
+                         d->P_total, ids, w, phys, partial, xq_tok, xs_tok, st));
+    MOE_TRY(launch_gemm1_pairs(xq_tok, xs_tok, phys, d->T, d->k, d->p0, pw1, pw1s, aq_p, as_p, counts, d->H, d->F,
+                               d->P_local, st));
+    MOE_TRY(launch_gemm2_pairs(aq_p, as_p, phys, d->T, d->k, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local, st));
+    MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys, d->p0, d->P_local, w, out, partial,
+                                 (d->T + kFrontTokens - 1) / kFrontTokens, d->P_total, load_hist, counts, offsets,
+                                 st));
+    return MOE_OK;
+  }
 
   MOE_TRY(launch_route(logits, d->T, d->E, d->k, ids, w, st));
   MOE_TRY(launch_count(d->T, d->k, ids, rep_count, rep_slots, d->R_max, d->token_id_base, phys, true, d->P_total,

@@ -31,6 +31,19 @@ hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* p
 hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* row_of_pair, const float* w,
                           uint16_t* out, hipStream_t st);
 
+// Small-M path (pair-indexed rows).  Front: routing, remap, per-16-token
+// chunk counts partial[ceil(T/16), P_total], and every token quantised into
+// xq_tok [T, H] / xs_tok [T, H/128].
+constexpr int kFrontTokens = 16;
+hipError_t launch_front(int T, int E, int k, int H, const float* logits, const uint16_t* x, const int32_t* rep_count,
+                        const int32_t* rep_slots, int R_max, uint32_t token_id_base, int P_total, int32_t* ids,
+                        float* w, int32_t* phys, int32_t* partial, uint8_t* xq_tok, uint8_t* xs_tok, hipStream_t st);
+// Combine of pair rows y [T*k, H], plus load_hist += the front's chunk
+// counts (load_hist nullable) and offsets from the per-slot counts GEMM1 wrote.
+hipError_t launch_combine_pairs(int T, int H, int k, const float* y, const int32_t* phys, int p0, int P_local,
+                                const float* w, uint16_t* out, const int32_t* partial, int nch, int P_total,
+                                int32_t* load_hist, const int32_t* counts, int32_t* offsets, hipStream_t st);
+
 // GEMM kernels (kernels_gemm.hip).  Weights are in the packed layout of
 // moe_layout.hpp; launch_pack converts one natural MXFP4 matrix set
 // [P, R, K/2] + [P, R, K/32] into it.
@@ -41,6 +54,17 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
                                hipStream_t st);
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                                const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
+// Pair-indexed GEMMs: each block lists its slot's pairs from phys [T*k].
+// GEMM1 reads per-token rows xq_tok/xs_tok and writes pair rows aq/as
+// [T*k, F]; GEMM2 reads those and writes pair rows y [T*k, H].  T <= 1024.
+constexpr int kPairMaxT = 1024;
+// GEMM1 also writes each slot's pair count into counts [P_local].
+hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, const int32_t* phys, int T, int k, int p0,
+                              const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int32_t* counts,
+                              int H, int F, int P_local, hipStream_t st);
+hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
+                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local,
+                              hipStream_t st);
 // Large-M: persistent tiled kernels (grid = one block per CU, items decoded
 // on the device from offsets).
 hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,

@@ -68,12 +68,28 @@ def run_forward(wl, path="auto", buf=None, hist_init=None, taps=True, dims_kw=No
         rows = int(c["offsets"][d.P_local])
         res.update(topk_ids=c["topk_ids"][:TK].reshape(d.T, d.k), topk_w=c["topk_w"][:TK].reshape(d.T, d.k),
                    phys_ids=c["phys_ids"][:TK].reshape(d.T, d.k), counts=c["counts"][:d.P_local],
-                   offsets=c["offsets"][:d.P_local + 1], row_of_pair=c["row_of_pair"][:TK],
-                   pair_of_row=c["pair_of_row"][:rows], rows=rows,
-                   xq=c["xq"][:rows * d.H].reshape(rows, d.H),
-                   xs=c["xs"][:rows * (d.H // 128)].reshape(rows, d.H // 128),
-                   aq=c["aq"][:rows * d.F].reshape(rows, d.F),
-                   as_=c["as_"][:rows * (d.F // 128)].reshape(rows, d.F // 128))
+                   offsets=c["offsets"][:d.P_local + 1], rows=rows)
+        nbh, nbf = d.H // 128, d.F // 128
+        if chosen == "small_m":
+            # pair-indexed intermediates; their bucket view follows from the GPU's
+            # own phys: slot s's rows are its pairs in ascending (t, j) order
+            phys = res["phys_ids"].ravel()
+            por = np.concatenate([np.nonzero(phys == d.p0 + s)[0] for s in range(d.P_local)] +
+                                 [np.zeros(0, np.int64)]).astype(np.int32)
+            rop = np.full(TK, -1, np.int32)
+            rop[por] = np.arange(len(por), dtype=np.int32)
+            xq_tok = c["xq_tok"][:d.T * d.H].reshape(d.T, d.H)
+            xs_tok = c["xs_tok"][:d.T * nbh].reshape(d.T, nbh)
+            aq_pair = c["aq_pair"][:TK * d.F].reshape(TK, d.F)
+            as_pair = c["as_pair"][:TK * nbf].reshape(TK, nbf)
+            res.update(row_of_pair=rop, pair_of_row=por, xq_tok=xq_tok, xs_tok=xs_tok,
+                       xq=xq_tok[por // d.k], xs=xs_tok[por // d.k], aq=aq_pair[por], as_=as_pair[por])
+        else:
+            res.update(row_of_pair=c["row_of_pair"][:TK], pair_of_row=c["pair_of_row"][:rows],
+                       xq=c["xq"][:rows * d.H].reshape(rows, d.H),
+                       xs=c["xs"][:rows * nbh].reshape(rows, nbh),
+                       aq=c["aq"][:rows * d.F].reshape(rows, d.F),
+                       as_=c["as_"][:rows * nbf].reshape(rows, nbf))
     return res
 
 
@@ -86,7 +102,7 @@ def oracle_front(wl) -> dict:
     xq_t, xs_t = om.quant_blocks(fm.bf16_to_f64(wl.x))
     tok = por // d.k
     return dict(topk_ids=ids, topk_w=w, phys_ids=phys, load_hist=hist, counts=counts, offsets=offsets,
-                row_of_pair=rop, pair_of_row=por, xq=xq_t[tok], xs=xs_t[tok])
+                row_of_pair=rop, pair_of_row=por, xq=xq_t[tok], xs=xs_t[tok], xq_tok=xq_t, xs_tok=xs_t)
 
 
 def check_front(res, ref, d):
@@ -100,6 +116,9 @@ def check_front(res, ref, d):
     assert np.array_equal(res["pair_of_row"], ref["pair_of_row"]), "pair_of_row"
     assert np.array_equal(res["xs"], ref["xs"]), "xs"
     assert np.array_equal(res["xq"], ref["xq"]), "xq"
+    if "xq_tok" in res:  # small-M: every token is quantised, local pairs or not
+        assert np.array_equal(res["xs_tok"], ref["xs_tok"]), "xs_tok"
+        assert np.array_equal(res["xq_tok"], ref["xq_tok"]), "xq_tok"
 
 
 def _ordinal(codes: np.ndarray) -> np.ndarray:

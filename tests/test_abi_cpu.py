@@ -59,6 +59,9 @@ def test_select_path_thresholds():
     assert mx.moe_select_path(_dims(T=1024, T_max=8192)) == "large_m"
     assert mx.moe_select_path(_dims(T=100, small_m_max=64, large_m_min=100)) == "large_m"
     assert mx.moe_select_path(_dims(T=64, small_m_max=64)) == "small_m"
+    # the small-input path lists each slot's pairs in one block: at most 1024 tokens
+    assert mx.moe_select_path(_dims(T=1024, T_max=8192, small_m_max=4096, large_m_min=8192)) == "small_m"
+    assert mx.moe_select_path(_dims(T=1025, T_max=8192, small_m_max=4096, large_m_min=8192)) == "staged"
 
 
 def test_status_strings():
@@ -98,6 +101,9 @@ def test_host_validation_before_launch():
     assert _forward_raw(_dims(H=200), GOOD, 0x100000, need)[0] == -1
     # bad path
     assert _forward_raw(d, GOOD, 0x100000, need, path=9)[0] == -1
+    # the small-input path beyond 1024 tokens is refused, not rerouted
+    big = _dims(T=1025, T_max=1025)
+    assert _forward_raw(big, GOOD, 0x100000, mx.moe_workspace_bytes(big), path=1)[0] == -2
 
 
 def test_zero_tokens_is_a_no_op():

@@ -73,6 +73,14 @@ def test_single_token_and_capacity_bucket():
     _full_check(wl)
 
 
+def test_small_m_at_its_token_limit():
+    # 1024 tokens each routed to all 16 experts: every slot lists 1024 pairs,
+    # the small-input path's capacity
+    wl = synth.make_custom(T=1024, H=256, F=128, E=16, k=16, P_local=16, seed=20)
+    res = _full_check(wl, "small_m")
+    assert res["rows"] == 1024 * 16
+
+
 def test_all_pairs_remote_gives_zero_output():
     wl = synth.make_custom(T=40, H=256, F=128, E=16, k=2, P_local=4, p0=12, seed=15)
     wl.logits[:, 12:] = -30.0          # nobody picks experts 12..15
@@ -92,11 +100,14 @@ def test_zero_tokens_writes_nothing():
     assert torch.all(out == 7) and torch.all(hist == 0)
 
 
-def test_component_calls_match_forward_bitwise():
+@pytest.mark.parametrize("path", ["small_m", "staged"])
+def test_component_calls_match_forward_bitwise(path):
+    # the pair-indexed small-input path and the bucketed component calls run
+    # the same arithmetic in the same order: equal bit for bit
     wl = synth.make_custom(T=130, H=512, F=256, E=16, k=4, P_local=8, p0=4, redundant=8, ranks=2, seed=17)
     d = mx.Dims.of(wl.dims)
     buf = P.upload(wl)
-    res = P.run_forward(wl, buf=buf)
+    res = P.run_forward(wl, buf=buf, path=path)
     TK, TMK = d.T * d.k, d.T_max * d.k
     z = lambda n, dt: torch.zeros(n, dtype=dt, device="cuda")  # noqa: E731
     ids, w, phys = z(TK, torch.int32), z(TK, torch.float32), z(TK, torch.int32)
@@ -191,9 +202,10 @@ def _big_check(wl, n_slots=3, n_tokens=24, path="auto"):
     return res
 
 
-def test_decode_share_512_tokens():
-    res = _big_check(synth.make("decode512"))
-    assert res["chosen"] == "small_m"
+@pytest.mark.parametrize("path", ["auto", "staged"])
+def test_decode_share_512_tokens(path):
+    res = _big_check(synth.make("decode512"), path=path)
+    assert res["chosen"] == ("small_m" if path == "auto" else path)
 
 
 def test_prefill_share_8192_tokens():
