@@ -203,6 +203,27 @@ int moe_grouped_gemm2_combine(const moe_dims_t* dims, const uint8_t* aq, const u
                               const int32_t* row_of_pair, const float* topk_w, uint16_t* out,
                               void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* a5 on the small-input path's pair-indexed rows (what MOE_PATH_SMALL_M runs
+ * between its front end and GEMM2) [sglang PR 47065, intro].  Same arithmetic
+ * as moe_grouped_gemm1_swiglu; the rows of slot s are the pairs p (ascending)
+ * with phys_ids[p] == p0 + s, listed by each block itself.  Inputs: per-token
+ * activations xq_tok u8 [T, H] / xs_tok u8 [T, H/128] (the a4 rule) and
+ * phys_ids [T*k]; outputs: act rows aq_pair u8 [T*k, F] / as_pair
+ * u8 [T*k, F/128] (rows of local pairs only; others untouched) and
+ * counts i32 [P_local].  T <= 1024, else MOE_ERR_UNSUPPORTED.  No workspace. */
+int moe_grouped_gemm1_swiglu_pairs(const moe_dims_t* dims, const uint8_t* xq_tok, const uint8_t* xs_tok,
+                                   const int32_t* phys_ids, const uint8_t* pw1, const uint8_t* pw1s,
+                                   uint8_t* aq_pair, uint8_t* as_pair, int32_t* counts, moe_stream_t stream);
+
+/* a6 + a7 on pair-indexed rows: y_p = W2_s dequant(aq_pair_p) for every local
+ * pair p (f32, in the workspace), then out as in moe_grouped_gemm2_combine
+ * with row(t, j) = t*k + j; `offsets` i32 [P_local + 1] receives the
+ * exclusive scan of `counts`.  T <= 1024, else MOE_ERR_UNSUPPORTED. */
+int moe_grouped_gemm2_combine_pairs(const moe_dims_t* dims, const uint8_t* aq_pair, const uint8_t* as_pair,
+                                    const int32_t* phys_ids, const uint8_t* pw2, const uint8_t* pw2s,
+                                    const float* topk_w, const int32_t* counts, int32_t* offsets, uint16_t* out,
+                                    void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
 /* The whole layer, a1..a7, on `path` (MOE_PATH_AUTO: moe_select_path).
  * rep_count / rep_slots describe the replica table; load_hist (nullable) is
  * accumulated as in a2 (pass NULL in decode: recording is prefill-only

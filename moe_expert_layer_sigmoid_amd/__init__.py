@@ -27,7 +27,8 @@ PATH_NAMES = {v: k for k, v in PATHS.items()}
 EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_packed_bytes",
            "moe_pack_weights", "moe_route",
            "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
-           "moe_grouped_gemm2_combine", "moe_forward")
+           "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
+           "moe_forward")
 
 
 class MoeError(RuntimeError):
@@ -87,10 +88,13 @@ def lib() -> ctypes.CDLL:
         L.moe_quant_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_grouped_gemm1_swiglu.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_grouped_gemm2_combine.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_grouped_gemm1_swiglu_pairs.argtypes = [D, P, P, P, P, P, P, P, P, P]
+        L.moe_grouped_gemm2_combine_pairs.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_forward.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps),
                                   ctypes.POINTER(ctypes.c_int), P, ctypes.c_size_t, P]
         for n in ("moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
-                  "moe_grouped_gemm2_combine", "moe_forward"):
+                  "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
+                  "moe_forward"):
             getattr(L, n).restype = I
         _lib_handle = L
     return _lib_handle
@@ -233,6 +237,31 @@ def moe_grouped_gemm2_combine(d: Dims, aq, as_, offsets, pw2, pw2s, row_of_pair,
         _ptr(row_of_pair, "row_of_pair", i32, TK), _ptr(topk_w, "topk_w", f32, TK),
         _ptr(out, "out", _bf16(out), d.T * d.H), _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
     _check("moe_grouped_gemm2_combine", rc)
+
+
+def moe_grouped_gemm1_swiglu_pairs(d: Dims, xq_tok, xs_tok, phys_ids, pw1, pw1s, aq_pair, as_pair, counts,
+                                   stream=None):
+    TK = d.T * d.k
+    rc = lib().moe_grouped_gemm1_swiglu_pairs(
+        ctypes.byref(d), _ptr(xq_tok, "xq_tok", u8, d.T * d.H), _ptr(xs_tok, "xs_tok", u8, d.T * (d.H // 128)),
+        _ptr(phys_ids, "phys_ids", i32, TK),
+        _ptr(pw1, "pw1", u8, moe_packed_bytes(d, 0)), _ptr(pw1s, "pw1s", u8, moe_packed_bytes(d, 1)),
+        _ptr(aq_pair, "aq_pair", u8, TK * d.F), _ptr(as_pair, "as_pair", u8, TK * (d.F // 128)),
+        _ptr(counts, "counts", i32, d.P_local), _stream(stream))
+    _check("moe_grouped_gemm1_swiglu_pairs", rc)
+
+
+def moe_grouped_gemm2_combine_pairs(d: Dims, aq_pair, as_pair, phys_ids, pw2, pw2s, topk_w, counts, offsets, out, ws,
+                                    stream=None):
+    TK = d.T * d.k
+    rc = lib().moe_grouped_gemm2_combine_pairs(
+        ctypes.byref(d), _ptr(aq_pair, "aq_pair", u8, TK * d.F), _ptr(as_pair, "as_pair", u8, TK * (d.F // 128)),
+        _ptr(phys_ids, "phys_ids", i32, TK),
+        _ptr(pw2, "pw2", u8, moe_packed_bytes(d, 2)), _ptr(pw2s, "pw2s", u8, moe_packed_bytes(d, 3)),
+        _ptr(topk_w, "topk_w", f32, TK), _ptr(counts, "counts", i32, d.P_local),
+        _ptr(offsets, "offsets", i32, d.P_local + 1), _ptr(out, "out", _bf16(out), d.T * d.H),
+        _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
+    _check("moe_grouped_gemm2_combine_pairs", rc)
 
 
 def make_taps(d: Dims, device="cuda") -> Dict[str, torch.Tensor]:

@@ -113,12 +113,15 @@ struct SStage {
   V8 b[2];
 };
 
-__device__ __forceinline__ void s_load(SStage& S, const SOps& O, int st) {
-  const uint32_t wo = (uint32_t)st * 2048, xo = (uint32_t)st * 256;
+// Operands of K step st; `gofs` moves the weight tiles to another group of
+// the wave's tiles (a uniform byte offset).
+template <int WAUX>
+__device__ __forceinline__ void s_load(SStage& S, const SOps& O, int st, uint32_t gofs = 0) {
+  const uint32_t wo = (uint32_t)st * 2048 + gofs, xo = (uint32_t)st * 256;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    S.a[rt][0] = buf_load16(O.w, O.wt[rt], wo);
-    S.a[rt][1] = buf_load16(O.w, O.wt[rt] + 1024, wo);
+    S.a[rt][0] = buf_load16_p<WAUX>(O.w, O.wt[rt], wo);
+    S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wt[rt] + 1024, wo);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -131,10 +134,10 @@ struct SScales {
   int lo[4], hi[4];  // steps 4q, 4q+1 (lo) and 4q+2, 4q+3 (hi) of each tile
 };
 
-__device__ __forceinline__ void s_load_scales(SScales& C, const SOps& O, int q) {
+__device__ __forceinline__ void s_load_scales(SScales& C, const SOps& O, int q, uint32_t gofs = 0) {
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const v2i v = buf_load8(O.ws, O.wst[rt], (uint32_t)q * 512);
+    const v2i v = buf_load8(O.ws, O.wst[rt], (uint32_t)q * 512 + gofs);
     C.lo[rt] = v.x;
     C.hi[rt] = v.y;
   }
@@ -156,34 +159,79 @@ __device__ __forceinline__ void s_mma(v4f (&acc)[4], const SStage& S, const SSca
   }
 }
 
-// All S4 (a multiple of 4) steps of one token tile.  Operand stages run two
-// steps ahead, scale quads one quad ahead; the loop has no branches (its last
-// loads re-read the final steps and are never used).
-__device__ __forceinline__ void stream_tile(v4f (&acc)[4], const SOps& O, int S4) {
+// One token tile against G groups of four weight tiles each (group g at
+// byte offsets g * gd in the data and g * sgd in the scales), streamed back
+// to back: all S4 (a multiple of 4) K steps of group 0, then of group 1, ...
+// Operand stages run two steps ahead and scale quads one quad ahead across
+// group boundaries, so the pipeline never drains between groups; the loop has
+// no branches (its last loads re-read the final steps and are never used).
+// After a group's last step epi(g, acc) consumes its results and acc restarts
+// at zero.  WAUX: cache policy of the weight loads.
+template <int WAUX, int G, typename Epi>
+__device__ __forceinline__ void stream_groups(v4f (&acc)[4], const SOps& O, int S4, uint32_t gd, uint32_t sgd,
+                                              Epi&& epi) {
   SStage s0, s1;
   SScales c0, c1;
-  const int nq = S4 / 4;
-  s_load_scales(c0, O, 0);
-  s_load(s0, O, 0);
-  s_load(s1, O, 1);
-  s_load_scales(c1, O, min(1, nq - 1));
-  for (int st = 0; st < S4; st += 4) {
-    const int sb0 = *reinterpret_cast<const int*>(O.sxs + 2 * st);
-    const int sb1 = *reinterpret_cast<const int*>(O.sxs + 2 * st + 4);
-    s_mma<0>(acc, s0, c0, sb0);
-    s_load(s0, O, min(st + 2, S4 - 2));
-    s_mma<1>(acc, s1, c0, sb0);
-    s_load(s1, O, min(st + 3, S4 - 1));
-    s_mma<2>(acc, s0, c0, sb1);
-    s_load(s0, O, min(st + 4, S4 - 2));
-    s_mma<3>(acc, s1, c0, sb1);
-    s_load(s1, O, min(st + 5, S4 - 1));
-    c0 = c1;
-    s_load_scales(c1, O, min(st / 4 + 2, nq - 1));
+  const int nq = S4 / 4, NQ = G * nq, V = G * S4;
+  static_assert(G == 1 || G == 2, "one or two groups");
+  auto ld = [&](SStage& S, int v) {
+    const int g = (G > 1 && v >= S4) ? 1 : 0;
+    s_load<WAUX>(S, O, v - g * S4, g ? gd : 0u);
+  };
+  auto ldsc = [&](SScales& C, int q) {
+    const int g = (G > 1 && q >= nq) ? 1 : 0;
+    s_load_scales(C, O, q - g * nq, g ? sgd : 0u);
+  };
+  ldsc(c0, 0);
+  ld(s0, 0);
+  ld(s1, 1);
+  ldsc(c1, min(1, NQ - 1));
+#pragma unroll 1
+  for (int g = 0; g < G; ++g) {
+    for (int q = 0; q < nq; ++q) {
+      const int st = 4 * q, v = g * S4 + st, vq = g * nq + q;
+      const int sb0 = *reinterpret_cast<const int*>(O.sxs + 2 * st);
+      const int sb1 = *reinterpret_cast<const int*>(O.sxs + 2 * st + 4);
+      s_mma<0>(acc, s0, c0, sb0);
+      ld(s0, min(v + 2, V - 2));
+      s_mma<1>(acc, s1, c0, sb0);
+      ld(s1, min(v + 3, V - 1));
+      s_mma<2>(acc, s0, c0, sb1);
+      ld(s0, min(v + 4, V - 2));
+      s_mma<3>(acc, s1, c0, sb1);
+      ld(s1, min(v + 5, V - 1));
+      c0 = c1;
+      ldsc(c1, min(vq + 2, NQ - 1));
+    }
+    epi(g, acc);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 }
 
+// One group: all S4 steps of one token tile, results left in acc.
+template <int WAUX>
+__device__ __forceinline__ void stream_tile(v4f (&acc)[4], const SOps& O, int S4) {
+  v4f res[4];
+  stream_groups<WAUX, 1>(acc, O, S4, 0u, 0u, [&](int, const v4f(&a)[4]) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) res[rt] = a[rt];
+  });
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) acc[rt] = res[rt];
+}
+
 constexpr int kMaxSteps = 64;    // K <= 16384
+
+// Cache policy of the streamed weight loads: non-temporal (each weight byte
+// is read once per call).  Measured on the decode share (512 tokens, 48
+// slots): GEMM1 5.4 -> 6.3 TB/s, GEMM2 (512-row blocks) 4.9 -> 5.2 TB/s.
+#ifndef MOE_G1_WAUX
+#define MOE_G1_WAUX 2
+#endif
+#ifndef MOE_G2_WAUX
+#define MOE_G2_WAUX 2
+#endif
 constexpr int kPairRows = kPairMaxT;  // rows of one slot on the pair-indexed path
 
 // The pairs (t, j) whose physical slot is q, ascending, into list[0, cap);
@@ -356,7 +404,7 @@ __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restri
     v4f acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_tile(acc, O, S4);
+    stream_tile<MOE_G1_WAUX>(acc, O, S4);
     // SwiGLU: acc[0]/acc[2] are gate/up of columns f0 + 4g + r, acc[1]/acc[3] of f0 + 16 + 4g + r
     float act[8];
 #pragma unroll
@@ -386,10 +434,14 @@ __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// a6: one block per (local slot s, 256-row block of H).  Wave w owns rows
-// hb*256 + 64w + [0, 64) as four 16-row tiles; y rows are f32 [rows, H]
-// (bucketed rows, or pair rows with the act rows pair-indexed too).
+// a6: one block per (local slot s, 512-row block of H).  Wave w owns rows
+// hb*512 + 128w + [0, 128) as two groups of four 16-row tiles, streamed back
+// to back (512-row blocks fill the chip in one round at three blocks per CU:
+// 7168 / 512 * 48 slots = 672 blocks).  y rows are f32 [rows, H] (bucketed
+// rows, or pair rows with the act rows pair-indexed too).
 // ---------------------------------------------------------------------------
+constexpr int kG2Rows = 512;
+
 template <bool PAIRS>
 __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restrict__ aq,
                                                          const uint8_t* __restrict__ as_,
@@ -401,7 +453,7 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
   __shared__ __align__(16) uint8_t s_xs[16 * 2 * kMaxSteps];
   __shared__ int s_list[PAIRS ? kPairRows : 1];
   __shared__ int s_cnt[2][4];
-  const int nhb = (H + 255) / 256;
+  const int nhb = (H + kG2Rows - 1) / kG2Rows;
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nhb, hb = item - s * nhb;
   const SlotRows<PAIRS> R = slot_rows<PAIRS>(offsets, phys, np, p0 + s, s, 1, s_list, s_cnt);
@@ -409,8 +461,8 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
   if (n <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int h0 = hb * 256 + wave * 64;
-  const bool live = h0 < H;  // wave-uniform; H is a multiple of 128 so a live wave has 4 full tiles
+  const int h0 = hb * kG2Rows + wave * 128;
+  const bool live = h0 < H;  // wave-uniform; H is a multiple of 128 so a live wave has 8 full tiles
   const PackGeom G = pack_geom((uint32_t)H, (uint32_t)F);
   const int S4 = (int)G.steps;
   const int nb = F / kActBlock;
@@ -423,6 +475,7 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
     O.wt[rt] = tile * (uint32_t)G.data_tile + 16u * lane;
     O.wst[rt] = tile * (uint32_t)G.scale_tile + 8u * lane;
   }
+  const uint32_t gd = 4u * (uint32_t)G.data_tile, sgd = 4u * (uint32_t)G.scale_tile;
   for (int tt0 = 0; tt0 < n; tt0 += 16) {
     const int tok = tt0 + l16;
     const bool tv = tok < n;
@@ -433,16 +486,17 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
     if (!live) continue;
     token_operand<PAIRS>(O, aq, R, tt0, nrow, nsrc, F, l16, g);
     O.sxs = s_xs + (tv ? l16 : 0) * 2 * S4;
+    float* yr = tv ? y + (size_t)R.dst(tok) * H + h0 + 4 * g : nullptr;
     v4f acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_tile(acc, O, S4);
-    if (tv) {
-      float* yr = y + (size_t)R.dst(tok) * H + h0 + 4 * g;
+    stream_groups<MOE_G2_WAUX, 2>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4]) {
+      if (tv) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        *reinterpret_cast<float4*>(yr + 16 * rt) = make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]);
-    }
+        for (int rt = 0; rt < 4; ++rt)
+          *reinterpret_cast<float4*>(yr + 64 * grp + 16 * rt) = make_float4(a[rt][0], a[rt][1], a[rt][2], a[rt][3]);
+      }
+    });
   }
 }
 
@@ -456,7 +510,7 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
 
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                                const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
-  k_gemm2_stream<false><<<P_local * ((H + 255) / 256), 256, 0, st>>>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y,
+  k_gemm2_stream<false><<<P_local * ((H + kG2Rows - 1) / kG2Rows), 256, 0, st>>>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y,
                                                                      H, F);
   return hipGetLastError();
 }
@@ -472,7 +526,7 @@ hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, cons
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local,
                               hipStream_t st) {
-  k_gemm2_stream<true><<<P_local * ((H + 255) / 256), 256, 0, st>>>(aq, as, nullptr, phys, T * k, p0, T * k, pw2,
+  k_gemm2_stream<true><<<P_local * ((H + kG2Rows - 1) / kG2Rows), 256, 0, st>>>(aq, as, nullptr, phys, T * k, p0, T * k, pw2,
                                                                     pw2s, y, H, F);
   return hipGetLastError();
 }

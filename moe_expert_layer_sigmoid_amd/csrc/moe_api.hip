@@ -247,6 +247,41 @@ int moe_grouped_gemm2_combine(const moe_dims_t* d, const uint8_t* aq, const uint
   return MOE_OK;
 }
 
+int moe_grouped_gemm1_swiglu_pairs(const moe_dims_t* d, const uint8_t* xq_tok, const uint8_t* xs_tok,
+                                   const int32_t* phys_ids, const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq_pair,
+                                   uint8_t* as_pair, int32_t* counts, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(xq_tok) || !dev_ok(xs_tok) || !dev_ok(phys_ids) || !dev_ok(pw1) || !dev_ok(pw1s) ||
+      !dev_ok(aq_pair) || !dev_ok(as_pair) || !dev_ok(counts))
+    return MOE_ERR_INVALID_ARG;
+  if (d->T > kPairMaxT) return MOE_ERR_UNSUPPORTED;
+  if (d->T == 0) return MOE_OK;
+  return hip_status(launch_gemm1_pairs(xq_tok, xs_tok, phys_ids, d->T, d->k, d->p0, pw1, pw1s, aq_pair, as_pair,
+                                       counts, d->H, d->F, d->P_local, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm2_combine_pairs(const moe_dims_t* d, const uint8_t* aq_pair, const uint8_t* as_pair,
+                                    const int32_t* phys_ids, const uint8_t* pw2, const uint8_t* pw2s,
+                                    const float* topk_w, const int32_t* counts, int32_t* offsets, uint16_t* out,
+                                    void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(aq_pair) || !dev_ok(as_pair) || !dev_ok(phys_ids) || !dev_ok(pw2) || !dev_ok(pw2s) ||
+      !dev_ok(topk_w) || !dev_ok(counts) || !dev_ok(offsets) || !dev_ok(out))
+    return MOE_ERR_INVALID_ARG;
+  if (d->T > kPairMaxT) return MOE_ERR_UNSUPPORTED;
+  if ((rc = check_ws(d, ws, ws_bytes))) return rc;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  float* y = at<float>(ws, layout_of(d).y);
+  MOE_TRY(launch_gemm2_pairs(aq_pair, as_pair, phys_ids, d->T, d->k, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local,
+                             st));
+  MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys_ids, d->p0, d->P_local, topk_w, out, nullptr, 0,
+                               d->P_total, nullptr, counts, offsets, st));
+  return MOE_OK;
+}
+
 int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const float* logits, const uint8_t* pw1,
                 const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rep_count,
                 const int32_t* rep_slots, int32_t* load_hist, uint16_t* out, const moe_taps_t* taps,

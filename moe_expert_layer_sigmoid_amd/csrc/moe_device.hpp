@@ -82,6 +82,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// 16-byte load with cache-policy bits `AUX` (2: non-temporal, for data read
+// once such as streamed weights).
+template <int AUX>
+__device__ __forceinline__ v4i buf_load16_p(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
 __device__ __forceinline__ v2i buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }

@@ -135,6 +135,33 @@ def test_component_calls_match_forward_bitwise(path):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), res["out"])
 
 
+def test_pair_components_match_small_m_forward_bitwise():
+    wl = synth.make_custom(T=130, H=512, F=256, E=16, k=4, P_local=8, p0=4, redundant=8, ranks=2, seed=17)
+    d = mx.Dims.of(wl.dims)
+    buf = P.upload(wl)
+    tp = mx.make_taps(d)
+    out_f = torch.full((d.T, d.H), -1, dtype=torch.int16, device="cuda")
+    mx.moe_forward(d, buf["x"], buf["logits"], buf["w1"], buf["w1s"], buf["w2"], buf["w2s"], buf["rep_count"],
+                   buf["rep_slots"], out_f, mx.workspace(d), path="small_m", taps=tp)
+    TK = d.T * d.k
+    z = lambda n, dt: torch.zeros(n, dtype=dt, device="cuda")  # noqa: E731
+    aq, as_ = z(TK * d.F, torch.uint8), z(TK * d.F // 128, torch.uint8)
+    counts, offsets = z(d.P_local, torch.int32), z(d.P_local + 1, torch.int32)
+    out = torch.full((d.T, d.H), -1, dtype=torch.int16, device="cuda")
+    mx.moe_grouped_gemm1_swiglu_pairs(d, tp["xq_tok"], tp["xs_tok"], tp["phys_ids"], buf["w1"], buf["w1s"], aq, as_,
+                                      counts)
+    mx.moe_grouped_gemm2_combine_pairs(d, aq, as_, tp["phys_ids"], buf["w2"], buf["w2s"], tp["topk_w"], counts,
+                                       offsets, out, mx.workspace(d))
+    torch.cuda.synchronize()
+    local = np.isin(tp["phys_ids"].cpu().numpy()[:TK], np.arange(d.p0, d.p0 + d.P_local))
+    assert np.array_equal(counts.cpu().numpy(), tp["counts"].cpu().numpy())
+    assert np.array_equal(offsets.cpu().numpy(), tp["offsets"].cpu().numpy())
+    a1 = aq.cpu().numpy().reshape(TK, d.F)[local]
+    a2 = tp["aq_pair"].cpu().numpy()[:TK * d.F].reshape(TK, d.F)[local]
+    assert np.array_equal(a1, a2)
+    assert np.array_equal(out.cpu().numpy(), out_f.cpu().numpy())
+
+
 def test_deterministic_and_histogram_accumulates():
     wl = synth.make_custom(T=257, H=256, F=128, E=32, k=6, P_local=16, p0=8, redundant=8, ranks=2, seed=18)
     d = mx.Dims.of(wl.dims)
