@@ -531,294 +531,4 @@ hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_
   return hipGetLastError();
 }
 
-// ===========================================================================
-// Large-M path: persistent tiled kernel.
-//
-// Work item = (local slot s, token block of BM = 128 * TG rows, weight block
-// of 256 rows: 128 gate + 128 up columns for GEMM1, 256 rows of H for
-// GEMM2).  Items are listed per slot (token blocks from the slot's row count,
-// read on the device) and dealt to the 8 XCDs in contiguous ranges, so the
-// weight blocks of one token block run on one XCD and share its rows in L2.
-//
-// Block = 4 * TG waves; wave (wg, tg) owns four 16-row weight tiles (group
-// wg) against eight 16-token tiles (group tg): 32 accumulators of 16x16.
-// K advances 128 per stage (one MFMA per tile pair).  The token rows of a
-// stage (BM x 128 B) are staged through LDS, double-buffered, pitch 144 B so
-// that the 16 tokens a ds_read_b128 touches fall in distinct bank groups; the
-// weight tiles stream from HBM into registers two stages ahead.
-// ===========================================================================
-constexpr int kLPitch = 144;
-
-template <int TG>
-struct LShared {
-  uint8_t b[2][128 * TG * kLPitch];   // token stage buffers
-  uint8_t xs[128 * TG * 128];          // 128-column scales of the block's tokens (K <= 16384)
-  float amax[TG][4][128];              // GEMM1 requant: per-token amax of each weight group
-  int prefix[1025];                    // exclusive prefix of token blocks per slot
-};
-
-// Token block count prefix over slots, computed by every block (P_local <= 1024).
-template <int TG>
-__device__ __forceinline__ int block_prefix(LShared<TG>& S, const int32_t* offsets, int P_local) {
-  constexpr int BM = 128 * TG;
-  const int tid = threadIdx.x;
-  for (int p = tid; p < P_local; p += blockDim.x) {
-    const int n = offsets[p + 1] - offsets[p];
-    S.prefix[p + 1] = (n + BM - 1) / BM;
-  }
-  if (tid == 0) S.prefix[0] = 0;
-  __syncthreads();
-  if (tid == 0) {  // P_local serial adds: negligible next to one item
-    int run = 0;
-    for (int p = 1; p <= P_local; ++p) {
-      run += S.prefix[p];
-      S.prefix[p] = run;
-    }
-  }
-  __syncthreads();
-  return S.prefix[P_local];
-}
-
-template <int TG, bool G1>
-__global__ __launch_bounds__(256 * TG, 1) void k_tiled(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const int32_t* __restrict__ offsets,
-    int P_local, const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws, uint8_t* __restrict__ aq,
-    uint8_t* __restrict__ as_, float* __restrict__ y, int H, int F) {
-  constexpr int BM = 128 * TG;
-  __shared__ LShared<TG> S;
-  const int K = G1 ? H : F;
-  const int R = G1 ? 2 * F : H;
-  const int nblk = G1 ? F / kActBlock : (H + 255) / 256;
-  const int nb = K / kActBlock;      // 128-wide K stages (real)
-  const PackGeom Gm = pack_geom((uint32_t)R, (uint32_t)K);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
-  const int l16 = lane & 15, g = lane >> 4;
-  const int wg = wave & 3, tg = wave >> 2;
-
-  const int nitems = block_prefix<TG>(S, offsets, P_local) * nblk;
-  // contiguous item range per XCD; blocks of one XCD stride through it
-  const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, lb = blockIdx.x >> 3;
-  const int chunk = (nitems + 7) / 8;
-  const int i0 = xcd * chunk, i1 = min(nitems, i0 + chunk);
-
-  for (int item = i0 + lb; item < i1; item += nper) {
-    const int tb = item / nblk, wb = item - tb * nblk;
-    // slot of token block tb: last s with prefix[s] <= tb
-    int lo = 0, hi = P_local - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (S.prefix[mid] <= tb) lo = mid;
-      else hi = mid - 1;
-    }
-    const int s = lo;
-    const int bm = tb - S.prefix[s];
-    const int n = offsets[s + 1] - offsets[s];
-    const int r0 = offsets[s] + bm * BM;
-    const int nvalid = min(BM, n - bm * BM);
-
-    // weight tiles of this wave
-    int tile[4];
-    bool wlive = true;
-    if (G1) {
-      const int f0 = wb * kActBlock + wg * 32;
-      tile[0] = f0 / 16; tile[1] = f0 / 16 + 1; tile[2] = (F + f0) / 16; tile[3] = (F + f0) / 16 + 1;
-    } else {
-      const int h0 = wb * 256 + wg * 64;
-      wlive = h0 < H;  // H is a multiple of 128: a live wave has four full tiles
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) tile[rt] = wlive ? h0 / 16 + rt : 0;
-    }
-    const rsrc_t Wr = make_rsrc(pw + (size_t)s * Gm.data_slot, (uint32_t)Gm.data_slot);
-    const rsrc_t Sr = make_rsrc(pws + (size_t)s * Gm.scale_slot, (uint32_t)Gm.scale_slot);
-    uint32_t wt[4], wst[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      wt[rt] = (uint32_t)tile[rt] * (uint32_t)Gm.data_tile + 16u * lane;
-      wst[rt] = (uint32_t)tile[rt] * (uint32_t)Gm.scale_tile + 8u * lane;
-    }
-    const int ntt = min(8, max(0, (nvalid - tg * 128 + 15) / 16));  // token tiles of this wave
-
-    __syncthreads();  // the previous item is done with S.b / S.xs / S.amax
-    for (int i = tid; i < BM * nb; i += blockDim.x) {
-      const int t = i / nb, c = i - t * nb;
-      S.xs[t * nb + c] = t < nvalid ? xs[(size_t)(r0 + t) * nb + c] : (uint8_t)0;
-    }
-    // token stage loader: 16-byte chunks, 8 per token row; two register sets
-    // so that a stage's rows are loaded three stages before use and written
-    // to LDS one stage before use
-    const rsrc_t Xr = make_rsrc(xq + (size_t)r0 * K, (uint32_t)nvalid * K);
-    uint4 breg0[4], breg1[4];
-    auto b_load = [&](uint4 (&br)[4], int stg) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + j * 256 * TG;  // chunk: token c / 8, piece c % 8
-        const int t = c >> 3, pc = c & 7;
-        br[j] = __builtin_bit_cast(uint4, buf_load16(Xr, (uint32_t)t * K + pc * 16, (uint32_t)stg * 128));
-      }
-    };
-    auto b_store = [&](const uint4 (&br)[4], int buf) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + j * 256 * TG;
-        const int t = c >> 3, pc = c & 7;
-        *reinterpret_cast<uint4*>(&S.b[buf][t * kLPitch + pc * 16]) = br[j];
-      }
-    };
-    v4i a0[4], a1[4];
-    auto a_load = [&](v4i (&a)[4], int stg) {
-      const uint32_t so = (uint32_t)(stg >> 1) * 2048 + (uint32_t)(stg & 1) * 1024;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a[rt] = buf_load16(Wr, wt[rt], so);
-    };
-    v2i scur[4], snext[4];
-    auto s_loadq = [&](v2i (&sc)[4], int grp) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) sc[rt] = buf_load8(Sr, wst[rt], (uint32_t)grp * 512);
-    };
-
-    v4f acc[4][8];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const int ngrp = Gm.steps / 4;  // scale groups of 8 stages
-    // prologue: rows of stages 0 and 1 to LDS, stage 2 in flight; weights of stages 0, 1
-    b_load(breg0, 0);
-    if (nb > 1) b_load(breg1, 1);
-    s_loadq(scur, 0);
-    s_loadq(snext, min(1, ngrp - 1));
-    if (wlive) {
-      a_load(a0, 0);
-      if (nb > 1) a_load(a1, 1);
-    }
-    b_store(breg0, 0);
-    if (nb > 1) b_store(breg1, 1);
-    if (nb > 2) b_load(breg0, 2);
-
-    auto stage = [&](const v4i (&a)[4], int stg) {
-      const int buf = stg & 1;
-      if (wlive) {
-        const int sh = 8 * (stg & 3);
-        int sa[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) sa[rt] = (int)((uint32_t)((stg & 4) ? scur[rt].y : scur[rt].x) >> sh);
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          if (tt >= ntt) continue;  // wave-uniform
-          const int tok = tg * 128 + tt * 16 + l16;
-          const uint8_t* bp = &S.b[buf][tok * kLPitch + g * 16];
-          V8 b;
-          b.h[0] = *reinterpret_cast<const v4i*>(bp);
-          b.h[1] = *reinterpret_cast<const v4i*>(bp + 64);
-          const int sb = S.xs[tok * nb + stg];
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[rt][tt] = mfma_ij<0, 0>(a[rt], b.v, acc[rt][tt], sa[rt], sb);
-          // keep the operand reads of one token tile next to its MFMAs
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-    // Stage stg reads LDS buffer stg & 1.  At its start (after the barrier)
-    // the rows of stage stg + 1 go from registers to the other buffer, whose
-    // readers (stage stg - 1) are past the barrier; the rows of stage stg + 3
-    // are requested into the register set just emptied.
-    for (int stg = 0; stg < nb; stg += 2) {
-      __syncthreads();
-      if (stg > 0 && stg + 1 < nb) b_store(breg1, 1);
-      if (stg + 3 < nb) b_load(breg1, stg + 3);
-      stage(a0, stg);
-      if (wlive && stg + 2 < nb) a_load(a0, stg + 2);
-      if (stg + 1 < nb) {
-        __syncthreads();
-        if (stg + 2 < nb) b_store(breg0, 0);
-        if (stg + 4 < nb) b_load(breg0, stg + 4);
-        stage(a1, stg + 1);
-        if (wlive && stg + 3 < nb) a_load(a1, stg + 3);
-      }
-      if (((stg + 2) & 7) == 0) {  // next scale group
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) scur[rt] = snext[rt];
-        s_loadq(snext, min((stg + 2) / 8 + 1, ngrp - 1));
-      }
-    }
-
-    // ---- epilogue
-    if (G1) {
-      // SwiGLU in place: acc[0] / acc[1] become act of the gate tiles' columns
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[0][tt][r] = silu(acc[0][tt][r]) * acc[2][tt][r];
-          acc[1][tt][r] = silu(acc[1][tt][r]) * acc[3][tt][r];
-        }
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        float m = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m = fmaxf(m, fmaxf(fabsf(acc[0][tt][r]), fabsf(acc[1][tt][r])));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        if (g == 0) S.amax[tg][wg][tt * 16 + l16] = m;
-      }
-      __syncthreads();
-      const int nfb = F / kActBlock;
-      const int f0 = wb * kActBlock + wg * 32;
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int tl = tt * 16 + l16;
-        const int tok = tg * 128 + tl;
-        if (tt >= ntt || tok >= nvalid) continue;
-        const float am = fmaxf(fmaxf(S.amax[tg][0][tl], S.amax[tg][1][tl]),
-                               fmaxf(S.amax[tg][2][tl], S.amax[tg][3][tl]));
-        const int e = scale_exp(am);
-        uint8_t* ap = aq + (size_t)(r0 + tok) * F + f0 + 4 * g;
-        *reinterpret_cast<uint32_t*>(ap) = pack4_fp8(ldexpf(acc[0][tt][0], -e), ldexpf(acc[0][tt][1], -e),
-                                                     ldexpf(acc[0][tt][2], -e), ldexpf(acc[0][tt][3], -e));
-        *reinterpret_cast<uint32_t*>(ap + 16) = pack4_fp8(ldexpf(acc[1][tt][0], -e), ldexpf(acc[1][tt][1], -e),
-                                                          ldexpf(acc[1][tt][2], -e), ldexpf(acc[1][tt][3], -e));
-        if (wg == 0 && g == 0) as_[(size_t)(r0 + tok) * nfb + wb] = (uint8_t)(e + 127);
-      }
-    } else if (wlive) {
-      const int h0 = wb * 256 + wg * 64;
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int tok = tg * 128 + tt * 16 + l16;
-        if (tt >= ntt || tok >= nvalid) continue;
-        float* yr = y + (size_t)(r0 + tok) * H + h0 + 4 * g;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          *reinterpret_cast<float4*>(yr + 16 * rt) =
-              make_float4(acc[rt][tt][0], acc[rt][tt][1], acc[rt][tt][2], acc[rt][tt][3]);
-      }
-    }
-  }
-}
-
-static int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
-hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
-                              const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
-                              hipStream_t st) {
-  k_tiled<1, true><<<num_cus() / 8 * 8, 256, 0, st>>>(xq, xs, offsets, P_local, pw1, pw1s, aq, as, nullptr, H, F);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                              const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
-  k_tiled<1, false><<<num_cus() / 8 * 8, 256, 0, st>>>(aq, as, offsets, P_local, pw2, pw2s, nullptr, nullptr, y, H,
-                                                       F);
-  return hipGetLastError();
-}
-
 }  // namespace moe

@@ -126,7 +126,7 @@ moe_path_t moe_select_path(const moe_dims_t* d) {
   const int small = d->small_m_max > 0 ? d->small_m_max : 512;
   const int large = d->large_m_min > 0 ? d->large_m_min : 1024;
   if (d->T <= small && d->T <= kPairMaxT) return MOE_PATH_SMALL_M;
-  if (d->T >= large) return MOE_PATH_LARGE_M;
+  if (d->T >= large && tiled_fits(d->H, d->F, d->P_local)) return MOE_PATH_LARGE_M;
   return MOE_PATH_STAGED;
 }
 
@@ -302,6 +302,7 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
   if ((rc = check_ws(d, ws, ws_bytes))) return rc;
   const moe_path_t p = path == MOE_PATH_AUTO ? moe_select_path(d) : path;
   if (p == MOE_PATH_SMALL_M && d->T > kPairMaxT) return MOE_ERR_UNSUPPORTED;
+  if (p == MOE_PATH_LARGE_M && !tiled_fits(d->H, d->F, d->P_local)) return MOE_ERR_UNSUPPORTED;
   if (chosen) *chosen = p;
   if (d->T == 0) return MOE_OK;
 

@@ -65,6 +65,11 @@ hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, cons
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local,
                               hipStream_t st);
+// Large-M: persistent tiled kernels.  Their LDS (operand rings plus the
+// block's token scales) must fit a CU's 160 KB, which holds for
+// H, F <= 8192: tiled_fits(H, F, P_local).
+constexpr size_t kTiledLdsMax = 160 * 1024;
+bool tiled_fits(int H, int F, int P_local);
 // Large-M: persistent tiled kernels (grid = one block per CU, items decoded
 // on the device from offsets).
 hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
