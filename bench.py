@@ -125,6 +125,83 @@ def run_gpu(workload: str, steps: int, warmup: int, copies: int):
                 gemm1_us=g1_us)
 
 
+def _time(fn, steps: int, warmup: int, stream) -> float:
+    """Average milliseconds of fn(i) over `steps` calls after `warmup`, by
+    events on the stream the work is launched on."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_sweep(steps: int, warmup: int, copies: int, only=None):
+    """The token-count sweep (decode-share shapes, AUTO path at each T) and
+    the EP-shaped prefill share (8 ranks x 8192 tokens into this GPU's 48
+    experts, LARGE_M).  One JSON line per point on stdout."""
+    import torch
+    import moe_expert_layer_sigmoid_amd as mx
+    import synth
+
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    base = synth.make_sweep(1)
+    d0 = mx.Dims.of(base.dims)
+    nat = [torch.from_numpy(a).to(dev) for a in (base.w1, base.w1s, base.w2, base.w2s)]
+    w = [mx.pack_weights(d0, *nat)]
+    del nat
+    for _ in range(copies - 1):
+        w.append(tuple(t.clone() for t in w[0]))
+
+    def point(wl, name, path="auto"):
+        d = mx.Dims.of(wl.dims)
+        x = torch.from_numpy(wl.x.view("int16")).to(dev)
+        logits = torch.from_numpy(wl.logits).to(dev)
+        rc = torch.from_numpy(wl.rep_count).to(dev)
+        rs = torch.from_numpy(wl.rep_slots).to(dev)
+        out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
+        ws = mx.workspace(d)
+        taps = mx.make_taps(d)
+        chosen = mx.moe_forward(d, x, logits, *w[0], rc, rs, out, ws, taps=taps, path=path)
+        torch.cuda.synchronize()
+        counts = taps["counts"].cpu().numpy()
+        touched, rows = int((counts > 0).sum()), int(counts.sum())
+        ms = _time(lambda i: mx.moe_forward(d, x, logits, *w[i % copies], rc, rs, out, ws, path=path),
+                   steps, warmup, st)
+        lay = layer_bytes(d, touched)
+        flops = 2 * rows * (2 * d.F * d.H + d.H * d.F)
+        rec = {"point": name, "T": d.T, "path": chosen, "touched_slots": touched, "rows": rows,
+               "ms_per_step": round(ms, 4), "tokens_per_s": round(d.T / (ms * 1e-3), 1),
+               "hbm_frac": round(lay / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        if chosen == "large_m":
+            # the two grouped GEMMs alone, through the component calls (bucketed rows)
+            g1 = _time(lambda i: mx.moe_grouped_gemm1_swiglu(d, taps["xq"], taps["xs"], taps["offsets"],
+                                                             w[i % copies][0], w[i % copies][1], taps["aq"],
+                                                             taps["as_"], ws, stream=st), steps, warmup, st)
+            g2c = _time(lambda i: mx.moe_grouped_gemm2_combine(d, taps["aq"], taps["as_"], taps["offsets"],
+                                                               w[i % copies][2], w[i % copies][3],
+                                                               taps["row_of_pair"], taps["topk_w"], out, ws,
+                                                               stream=st), steps, warmup, st)
+            f1 = 2 * rows * 2 * d.F * d.H
+            rec.update(gemm1_ms=round(g1, 4), gemm1_mfma_frac=round(f1 / (g1 * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                       gemm2_combine_ms=round(g2c, 4))
+        print(json.dumps(rec), flush=True)
+        del ws, taps, out
+
+    for T in synth.SWEEP_T:
+        if only is None or f"sweep_T{T}" in only:
+            point(synth.make_sweep(T, with_weights=False), f"sweep_T{T}")
+    if only is None or "prefill_ep8_rank_share" in only:
+        point(synth.make_ep_shaped(8, with_weights=False), "prefill_ep8_rank_share", path="large_m")
+
+
 def cpu_baseline(wl, n_slots: int):
     """The oracle (float64 NumPy) on a bounded sample: the whole front end for
     all tokens plus the expert work of the first ``n_slots`` local slots,
@@ -169,6 +246,11 @@ def main():
     ap.add_argument("--workload", default="decode512", help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slots", type=int, default=8)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: the token-count sweep and the EP-shaped prefill share, "
+                         "one JSON line per point")
+    ap.add_argument("--points", default=None,
+                    help="with --sweep: comma-separated point names (sweep_T<T>, prefill_ep8_rank_share)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB with torch (a plain copy kernel of "
                          "known size, for scaling HBM byte counters under rocprofv3 --pmc)")
@@ -177,6 +259,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported"}))
         sys.exit(2)
 
+    if args.sweep:
+        run_sweep(args.steps, args.warmup, args.copies,
+                  None if args.points is None else set(args.points.split(",")))
+        return
     if args.calibrate_copy_mib:
         import torch
         n = args.calibrate_copy_mib << 20

@@ -10,6 +10,7 @@ activation quantisation, GEMMs, SwiGLU, combine).
 from .inputs import (  # noqa: F401
     Dims,
     Workload,
+    SWEEP_T,
     WORKLOADS,
     dims_for,
     make,
