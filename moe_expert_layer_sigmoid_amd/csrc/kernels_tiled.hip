@@ -11,18 +11,20 @@
 // grid is one block per CU; each block walks items of its XCD's contiguous
 // range.
 //
-// Block = 4 waves, one block per CU: one wave per SIMD, so the 32
-// accumulator tiles live in AGPRs next to a deep operand pipeline in VGPRs.
-// Wave w owns four 16-row weight tiles (GEMM1: the gate and up tiles of 32
-// columns of F; GEMM2: 64 rows of H) against the eight 16-token tiles of the
-// block: 32 accumulators of 16x16 (128 registers).  K advances 128 per stage
-// (one V_MFMA_SCALE_F32_16X16X128_F8F6F4 per tile pair).
+// Block = kNW waves, one block per CU.  The block tile is 128 tokens x 256
+// weight rows; weight quarter wq = wave % 4 (GEMM1: the gate and up tiles of
+// 32 columns of F; GEMM2: 64 rows of H, four 16-row tiles) runs on SIMD wq,
+// and with kNW = 8 two waves share each SIMD, one per half of the block's
+// eight 16-token tiles, so that one wave's LDS and barrier waits are filled
+// by the other's MFMAs.  K advances 128 per stage (one
+// V_MFMA_SCALE_F32_16X16X128_F8F6F4 per tile pair).
 //  - Token rows: direct-to-LDS DMA (buffer_load_dwordx4 ... lds), a ring of
 //    kRing stages issued kRing - 1 stages ahead; each stage row of 128 bytes
 //    is stored with its eight 16-byte pieces XOR-swizzled so the B-operand
 //    reads of a 16-token tile hit distinct banks.
-//  - Weight tiles: streamed from HBM straight into registers (the packed
-//    layout is the MFMA operand order), three stages ahead.
+//  - Weight tiles (the packed layout is the MFMA operand order) and their
+//    scales: direct-to-LDS DMA into the same ring, read back with one
+//    ds_read_b128 per tile.
 //  - Stage barriers are bare s_barrier with explicit vmcnt waits: the
 //    generic workgroup barrier would drain every load in flight.
 
@@ -42,18 +44,35 @@ constexpr int kStage = kTM * 128;  // bytes of one token stage
 constexpr int kWStage = 16 * 1024; // bytes of one weight stage (16 tiles x 64 lanes x 16 B)
 constexpr int kSGroup = 16 * 512;  // bytes of one scale group (16 tiles, 8 stages)
 constexpr int kMaxStages = 64;     // K <= 8192
+constexpr int kNW = 8;             // waves per block: two per SIMD (measured 7% faster than one)
+constexpr int kWPS = kNW / 4;      // waves per SIMD = token groups of the block tile
+constexpr int kTT = 8 / kWPS;      // 16-token tiles per wave
+constexpr int kXI = 16 / kNW;      // token DMA instructions per wave per stage (1 KB each)
+constexpr int kWI = 4 / kWPS;      // weight DMA instructions per wave per stage
+constexpr int kSI = 2 / kWPS;      // scale DMA instructions per wave per scale group
 
-// DMA instructions a wave issues after a stage's own (4 token + 4 weight) by
-// the time that stage is consumed: two more stages of 8.  Scale-group DMA
-// only adds to the count, which keeps the wait sufficient.  (Scale groups are
-// issued four stages before their first use, with at least 24 DMA
-// instructions after them by then: complete under the same wait.)
-#define MOE_TILED_VMCNT "16"
+// vmcnt accounting.  A stage's DMA is waited for at the start of the stage
+// three later; after it the wave has issued two more stages of DMA (kXI +
+// kWI each) and, with kStageStores = 1 (GEMM2), one store per stage: three.
+// Scale-group DMA and token-scale loads only add to the count, which keeps
+// the wait sufficient.  (Scale groups are issued at least three stages
+// before their first use, with three stages of DMA after them by then.)
+template <bool G1>
+constexpr int kStageStores = G1 ? 0 : 1;
+template <bool G1>
+constexpr int kVmWait = 2 * (kXI + kWI) + 3 * kStageStores<G1>;
+// GEMM1's epilogue stores are issued after the DMA of the next item's first
+// three stages and, like them, count in vmcnt: every wave issues exactly
+// kEpiStores of them (rows past the item store out of the buffer's range,
+// which the hardware drops), so the waits of those three stages allow that
+// many more and never drain them.
+constexpr int kEpiStores = 3 * kTT;
 
 // Physical 16-byte piece of logical piece p in the stage row of the token at
-// position r (mod 16) of its tile: p ^ swz(r).  Eight consecutive tokens, and
-// sixteen, land on distinct bank groups.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// position r (mod 16) of its tile: p ^ swz(r).  Measured on gfx950 for the
+// B-operand reads (16 rows x one piece per ds_read_b128 quarter): r & 7 reads
+// at 1.6x the rate of an XOR that also folds in bit 3, and 3x unswizzled rows.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
@@ -111,7 +130,7 @@ struct TItem {
 };
 
 template <bool G1>
-__global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+__global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                     const int32_t* __restrict__ offsets, int P_local,
                                                     const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws,
                                                     uint8_t* __restrict__ aq, uint8_t* __restrict__ as_,
@@ -133,11 +152,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
   const int nst4 = (nst + 3) & ~3;       // stages run per item: whole ring turns
   const PackGeom Gm = pack_geom((uint32_t)R, (uint32_t)K);
   const int ngrp = (int)Gm.steps / 4;    // scale groups (8 stages each); 8 ngrp >= nst4
-  float* s_amax = reinterpret_cast<float*>(lds);            // [4][kTM]
+  float* s_amax = reinterpret_cast<float*>(lds);            // [4 weight quarters][kTM]
   int* s_pre = reinterpret_cast<int*>(s_amax + 4 * kTM);    // [P_local + 1] items before slot
   int* s_off = s_pre + P_local + 1;                         // [P_local + 1] bucket offsets
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave & 3, th = kWPS == 1 ? 0 : wave >> 2;  // weight quarter (SIMD), token group
   const int l16 = lane & 15, g = lane >> 4;
   const int sw = swz(l16);
 
@@ -162,10 +182,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
   if (i0 + lb >= i1) return;  // block-uniform: no item for this block
 
   // lane constants of the DMA offsets
-  uint32_t xt[4], xp[4];  // token DMA instruction wave + 4m: token row and byte offset of the lane's piece
+  uint32_t xt[kXI], xp[kXI];  // token DMA instruction wave + kNW m: token row and byte offset of the lane's piece
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int t = 8 * (wave + 4 * m) + (lane >> 3);
+  for (int m = 0; m < kXI; ++m) {
+    const int t = 8 * (wave + kNW * m) + (lane >> 3);
     xt[m] = (uint32_t)t;
     xp[m] = 16u * (uint32_t)((lane & 7) ^ swz(t & 15));
   }
@@ -197,13 +217,13 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
     it.r0 = __builtin_amdgcn_readfirstlane(s_off[s] + tb * kTM);
     it.nvalid = __builtin_amdgcn_readfirstlane(it.live ? min(kTM, n - tb * kTM) : 0);
     it.live = __builtin_amdgcn_readfirstlane(it.live);
-    it.wlive = it.live && (G1 || wb * kTN + wave * 64 < H);  // H is a multiple of 128
+    it.wlive = it.live && (G1 || wb * kTN + wq * 64 < H);  // H is a multiple of 128
     if (G1) {  // gate and up tiles of columns f0 .. f0 + 31
-      const int f0 = it.wb * kActBlock + wave * 32;
+      const int f0 = it.wb * kActBlock + wq * 32;
       it.tl[0] = f0 / 16;
       it.tl[1] = (F + f0) / 16;
     } else {   // rows h0 .. h0 + 63
-      const int h0 = it.wb * kTN + wave * 64;
+      const int h0 = it.wb * kTN + wq * 64;
       it.tl[0] = h0 / 16;
       it.tl[1] = h0 / 16 + 2;
     }
@@ -217,59 +237,63 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
     const uint32_t xlim = (uint32_t)it.nvalid * (uint32_t)K;
     const rsrc_t Xr = make_rsrc(xq + (size_t)it.r0 * K, xlim);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < kXI; ++m) {
       const uint32_t vo = (live && xt[m] < (uint32_t)it.nvalid) ? xt[m] * (uint32_t)K + xp[m] : xlim;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (lds_ptr_t)(slot + (wave + 4 * m) * 1024), 16, vo,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (lds_ptr_t)(slot + (wave + kNW * m) * 1024), 16, vo,
                                                live ? (uint32_t)q * 128u : 0u, 0, 0);
     }
   };
-  auto dma_w = [&](const TItem it, uint8_t* slot, int q) {  // this wave's four weight tiles of stage q
+  auto dma_w = [&](const TItem it, uint8_t* slot, int q) {  // this wave's share of its quarter's tiles of stage q
     const bool live = it.wlive && q < nst;
     const rsrc_t Wr = make_rsrc(pw + (size_t)it.s * Gm.data_slot, wlim);
     const uint32_t so = (uint32_t)(q >> 1) * 2048u + (uint32_t)(q & 1) * 1024u;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const uint32_t tile = (uint32_t)(it.tl[rt >> 1] + (rt & 1));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(Wr, (lds_ptr_t)(slot + wave * 4096 + rt * 1024), 16,
+    for (int i = 0; i < kWI; ++i) {
+      const int rt = th * kWI + i;  // tl[] picked by selects: a runtime index would put the item in scratch
+      const uint32_t tile = (uint32_t)(((rt >> 1) ? it.tl[1] : it.tl[0]) + (rt & 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Wr, (lds_ptr_t)(slot + wq * 4096 + rt * 1024), 16,
                                                live ? wlane : wlim, live ? tile * (uint32_t)Gm.data_tile + so : 0u, 0,
                                                kWeightNt);
     }
   };
-  auto dma_s = [&](const TItem it, int grp, int par) {  // this wave's scales of group grp into slot par
+  auto dma_s = [&](const TItem it, int grp, int par) {  // this wave's share of its quarter's scales of group grp
     const bool live = it.wlive && grp < ngrp;
     const rsrc_t Sr = make_rsrc(pws + (size_t)it.s * Gm.scale_slot, slim);
-    uint8_t* slot = sring + par * kSGroup + wave * 2048;
+    uint8_t* slot = sring + par * kSGroup + wq * 2048;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < kSI; ++i) {
+      const int h = th * kSI + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(Sr, (lds_ptr_t)(slot + h * 1024), 16, live ? slane : slim,
-                                               live ? (uint32_t)it.tl[h] * (uint32_t)Gm.scale_tile + (uint32_t)grp * 512u : 0u,
+                                               live ? (uint32_t)(h ? it.tl[1] : it.tl[0]) * (uint32_t)Gm.scale_tile + (uint32_t)grp * 512u : 0u,
                                                0, 0);
+    }
   };
   // The item's token scales, stage-major: byte tt of lane record [q][r] is
   // the scale of token 16 tt + r at stage q (one 8-byte read gives a lane all
-  // eight); stages past the data hold 0.  Two threads per token row.  Rows of
+  // eight); stages past the data hold 0.  kTPR threads per token row.  Rows of
   // a multiple of 4 bytes are fetched as dwords into registers well ahead of
   // use (relaxed atomic loads: issued where written, not sunk to the use);
   // other widths are read byte by byte when stored.
-  constexpr int kXsPer = kMaxStages / 8;  // dwords per thread
+  constexpr int kTPR = kNW * 64 / kTM;             // threads per token row
+  constexpr int kXsPer = kMaxStages / 4 / kTPR;    // dwords per thread
   const bool xs_dw = (nst & 3) == 0;
   auto xs_fetch = [&](const TItem it, uint32_t (&v)[kXsPer]) {
-    const int t = tid >> 1;
+    const int t = tid / kTPR;
     const bool ok = xs_dw && it.live && t < it.nvalid;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(xs + (size_t)(it.r0 + t) * nst);
 #pragma unroll
     for (int j = 0; j < kXsPer; ++j) {
-      const int d = (tid & 1) + 2 * j;  // dword of the row
+      const int d = (tid % kTPR) + kTPR * j;  // dword of the row
       v[j] = (ok && 4 * d < nst) ? __hip_atomic_load(src + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
     }
   };
   auto xs_store = [&](const TItem it, const uint32_t (&v)[kXsPer]) {
-    const int t = tid >> 1;
+    const int t = tid / kTPR;
     uint8_t* dst = s_xs + (t & 15) * 8 + (t >> 4);
     if (xs_dw) {
 #pragma unroll
       for (int j = 0; j < kXsPer; ++j) {
-        const int d = (tid & 1) + 2 * j;
+        const int d = (tid % kTPR) + kTPR * j;
         if (4 * d < nst4) {
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) dst[(4 * d + bb) * kTM] = (uint8_t)(v[j] >> (8 * bb));
@@ -278,15 +302,23 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
     } else {
       const bool ok = it.live && t < it.nvalid;
       const uint8_t* src = xs + (size_t)(it.r0 + t) * nst;
-      for (int c = tid & 1; c < nst4; c += 2) dst[c * kTM] = (ok && c < nst) ? src[c] : (uint8_t)0;
+      for (int c = tid % kTPR; c < nst4; c += kTPR) dst[c * kTM] = (ok && c < nst) ? src[c] : (uint8_t)0;
     }
   };
 
   const int o_lo = (g ^ sw) * 16, o_hi = ((g + 4) ^ sw) * 16;
   v2i sc[4];  // weight scales of the current group: byte q % 8 scales stage q
-  v4f acc[4][8];
+  v4f acc[4][kTT];
+  constexpr int kTile = 16 * 128;  // bytes of one 16-token tile of a stage
 
-  // all eight token tiles of stage q (tiles past the block's rows hold zeros)
+  // B operand (token tile tt of this wave's group) from the stage's rows
+  auto ldb = [&](V8T& b, uint32_t blo, uint32_t bhi, auto ttc) {
+    constexpr int o = decltype(ttc)::value * kTile;
+    b.h[0] = lds_read16_at<o>(blo);
+    b.h[1] = lds_read16_at<o>(bhi);
+  };
+
+  // this wave's kTT token tiles of stage q (tiles past the block's rows hold zeros)
   auto compute = [&](bool wlive, const uint8_t* xs_slot, const uint8_t* w_slot, int q) {
     if (!wlive) return;
     // LDS reads in issue order (they complete in order): weights (4), token
@@ -294,8 +326,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
     // before tile tt's MFMAs.  Tile tt's operands are complete once at most
     // the reads of the two later tiles are outstanding.  Addresses are one
     // register each plus immediate offsets.
-    const uint32_t aa = lds_addr(w_slot + wave * 4096 + lane * 16);
-    const uint32_t blo = lds_addr(xs_slot + l16 * 128 + o_lo), bhi = lds_addr(xs_slot + l16 * 128 + o_hi);
+    const uint32_t aa = lds_addr(w_slot + wq * 4096 + lane * 16);
+    const uint8_t* xg = xs_slot + th * kTT * kTile + l16 * 128;
+    const uint32_t blo = lds_addr(xg + o_lo), bhi = lds_addr(xg + o_hi);
     v4i a[4];
     a[0] = lds_read16_at<0>(aa);
     a[1] = lds_read16_at<1024>(aa);
@@ -303,44 +336,78 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
     a[3] = lds_read16_at<3072>(aa);
     const v2i sbw = lds_read8(s_xs + q * kTM + l16 * 8);
     V8T b[3];
-    b[0].h[0] = lds_read16_at<0>(blo);
-    b[0].h[1] = lds_read16_at<0>(bhi);
-    b[1].h[0] = lds_read16_at<2048>(blo);
-    b[1].h[1] = lds_read16_at<2048>(bhi);
+    ldb(b[0], blo, bhi, std::integral_constant<int, 0>{});
+    ldb(b[1], blo, bhi, std::integral_constant<int, 1>{});
     int sa[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) sa[rt] = (int)((uint32_t)((q & 4) ? sc[rt].y : sc[rt].x) >> (8 * (q & 3)));
     MOE_LGKM_WAIT(4);  // weights and token scales are in
     __builtin_amdgcn_sched_barrier(0);
-    int sb[8];
+    int sb[kTT];
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) sb[tt] = (int)(((uint32_t)(tt < 4 ? sbw.x : sbw.y) >> (8 * (tt & 3))) & 0xFFu);
+    for (int tt = 0; tt < kTT; ++tt) {
+      const int t8 = th * kTT + tt;  // byte of the 8-tile record
+      sb[tt] = (int)(((uint32_t)(t8 < 4 ? sbw.x : sbw.y) >> (8 * (t8 & 3))) & 0xFFu);
+    }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      if (tt + 2 < 8) {
-        constexpr int kTile = 16 * 128;
-        switch (tt) {  // immediate offsets of tile tt + 2
-          case 0: b[2].h[0] = lds_read16_at<2 * kTile>(blo); b[2].h[1] = lds_read16_at<2 * kTile>(bhi); break;
-          case 1: b[0].h[0] = lds_read16_at<3 * kTile>(blo); b[0].h[1] = lds_read16_at<3 * kTile>(bhi); break;
-          case 2: b[1].h[0] = lds_read16_at<4 * kTile>(blo); b[1].h[1] = lds_read16_at<4 * kTile>(bhi); break;
-          case 3: b[2].h[0] = lds_read16_at<5 * kTile>(blo); b[2].h[1] = lds_read16_at<5 * kTile>(bhi); break;
-          case 4: b[0].h[0] = lds_read16_at<6 * kTile>(blo); b[0].h[1] = lds_read16_at<6 * kTile>(bhi); break;
-          case 5: b[1].h[0] = lds_read16_at<7 * kTile>(blo); b[1].h[1] = lds_read16_at<7 * kTile>(bhi); break;
-        }
-      }
-      if (tt < 6) MOE_LGKM_WAIT(4);
-      else if (tt == 6) MOE_LGKM_WAIT(2);
+    auto tile = [&](auto ttc) {
+      constexpr int tt = decltype(ttc)::value;
+      if constexpr (tt + 2 < kTT) ldb(b[(tt + 2) % 3], blo, bhi, std::integral_constant<int, tt + 2>{});
+      if constexpr (tt + 2 < kTT) MOE_LGKM_WAIT(4);
+      else if constexpr (tt + 1 < kTT) MOE_LGKM_WAIT(2);
       else MOE_LGKM_WAIT(0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt][tt] = mfma_fp4_fp8<0>(a[rt], b[tt % 3].v, acc[rt][tt], sa[rt], sb[tt]);
       __builtin_amdgcn_sched_barrier(0);
+    };
+    tile(std::integral_constant<int, 0>{});
+    tile(std::integral_constant<int, 1>{});
+    tile(std::integral_constant<int, 2>{});
+    tile(std::integral_constant<int, 3>{});
+    if constexpr (kTT == 8) {
+      tile(std::integral_constant<int, kTT == 8 ? 4 : 0>{});
+      tile(std::integral_constant<int, kTT == 8 ? 5 : 0>{});
+      tile(std::integral_constant<int, kTT == 8 ? 6 : 0>{});
+      tile(std::integral_constant<int, kTT == 8 ? 7 : 0>{});
+    }
+  };
+
+  // GEMM2 writes an item's y tiles during the next item's stages, one
+  // 16x16 tile per stage and wave, instead of all at the item's end: the
+  // items of all CUs end together, and their y rows written at once stall
+  // every CU on the write burst (measured: 9.1k -> 3.4k clocks per item
+  // with the burst removed).  yst holds the previous item's results not yet
+  // stored, the next token tile first (a shift after every fourth store
+  // keeps every register index a constant); a store past the previous item
+  // (or with none) lands out of range and is dropped.
+  v4f yst[4][kTT];
+  rsrc_t Yp = make_rsrc(y, 0u);  // the previous item's rows
+  uint32_t yp_lane = 0;          // this lane's byte offset within them (tile 0, rt 0)
+  auto ystore = [&](auto rtc, int q) {  // tile (rt, q / 4) of the previous item; q % 4 == rt
+    constexpr int rt = decltype(rtc)::value;
+    const int tt = q >> 2;
+    const uint32_t off = tt < kTT ? yp_lane + (uint32_t)tt * 16u * (uint32_t)H * 4u + 64u * rt : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, yst[rt][0]), Yp, off, 0, 0);
+    if constexpr (rt == 3) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j + 1 < kTT; ++j) yst[r][j] = yst[r][j + 1];
+    }
+  };
+  auto ystore_rt = [&](int q) {  // runtime rt = q % 4
+    switch (q & 3) {
+      case 0: ystore(std::integral_constant<int, 0>{}, q); break;
+      case 1: ystore(std::integral_constant<int, 1>{}, q); break;
+      case 2: ystore(std::integral_constant<int, 2>{}, q); break;
+      default: ystore(std::integral_constant<int, 3>{}, q); break;
     }
   };
 
   // ---- first item: its token scales, first scale group and first stages
   TItem cur = decode(i0 + lb);
+  bool after_epi = false;  // GEMM1: an epilogue's stores are in flight (every item but the first)
   int gpar = 0;  // scale slot of the current item's group 0
   {
     uint32_t v[kXsPer];
@@ -349,12 +416,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
   }
   __syncthreads();
   dma_s(cur, 0, 0);
-  dma_x(cur, xring[0], 0);
-  dma_w(cur, wring[0], 0);
-  dma_x(cur, xring[1], 1);
-  dma_w(cur, wring[1], 1);
-  dma_x(cur, xring[2], 2);
-  dma_w(cur, wring[2], 2);
+#pragma unroll
+  for (int q = 0; q < kAhead; ++q) {
+    dma_x(cur, xring[q], q);
+    dma_w(cur, wring[q], q);
+    if constexpr (!G1) ystore(std::integral_constant<int, 0>{}, 4 * kTT);  // nothing yet: the per-stage count
+  }
 
   for (int item = i0 + lb; item < i1; item += nper) {
     // the next item: decoded now; its first stages and first scale group are
@@ -365,7 +432,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < kTT; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // one stage (ring slot u = q % kRing, a compile-time constant): wait for
     // its rows and weights (own DMA, then everyone's via the barrier, which
@@ -373,10 +440,13 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
     // this item or, past its end, of the next), compute stage q
     auto stage = [&](auto uc, int q) {
       constexpr int u = decltype(uc)::value;
-      asm volatile("s_waitcnt vmcnt(" MOE_TILED_VMCNT ")" ::: "memory");
+      if (G1 && after_epi && q < 3)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kVmWait<G1> + kEpiStores) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kVmWait<G1>) : "memory");
       bare_barrier();
       if ((q & 7) == 0 && cur.wlive) {  // a new scale group (its DMA was issued at least three stages ago)
-        const uint8_t* sp = sring + ((gpar + (q >> 3)) & 1) * kSGroup + wave * 2048 + lane * 8;
+        const uint8_t* sp = sring + ((gpar + (q >> 3)) & 1) * kSGroup + wq * 2048 + lane * 8;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) sc[rt] = lds_read8(sp + (rt >> 1) * 1024 + (rt & 1) * 512);
         MOE_LGKM_WAIT(0);
@@ -391,6 +461,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
         dma_x(nxt, xring[(u + kAhead) % kRing], q + kAhead - nst4);
         dma_w(nxt, wring[(u + kAhead) % kRing], q + kAhead - nst4);
       }
+      if constexpr (!G1) ystore(std::integral_constant<int, u>{}, q);  // q % 4 == u: stage loops start at multiples of 4
       compute(cur.wlive, xring[u], wring[u], q);
     };
     for (int q0 = 0; q0 < nst4 - 4; q0 += 4) {
@@ -411,55 +482,61 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
 
     // ---- epilogue (LDS exchanges use bare barriers: the next item's DMA
     // stays in flight)
-    const int ntt = (cur.nvalid + 15) / 16;
     if (G1) {
       // SwiGLU in place: acc[0] / acc[1] become act of the gate tiles' columns
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
+      for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           acc[0][tt][r] = silu(acc[0][tt][r]) * acc[2][tt][r];
           acc[1][tt][r] = silu(acc[1][tt][r]) * acc[3][tt][r];
         }
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
+      for (int tt = 0; tt < kTT; ++tt) {
         float m = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) m = fmaxf(m, fmaxf(fabsf(acc[0][tt][r]), fabsf(acc[1][tt][r])));
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
-        if (g == 0) s_amax[wave * kTM + tt * 16 + l16] = m;
+        if (g == 0) s_amax[wq * kTM + (th * kTT + tt) * 16 + l16] = m;
       }
       MOE_LGKM_WAIT(0);
       bare_barrier();
+      // stores through buffers sized to the item's rows: lanes past them are dropped
       const int nfb = F / kActBlock;
-      const int f0 = cur.wb * kActBlock + wave * 32;
+      const int f0 = cur.wb * kActBlock + wq * 32;
+      const rsrc_t Ar = make_rsrc(aq + (size_t)cur.r0 * F, (uint32_t)cur.nvalid * (uint32_t)F);
+      const uint32_t slim_as = (uint32_t)cur.nvalid * (uint32_t)nfb;
+      const rsrc_t Sr = make_rsrc(as_ + (size_t)cur.r0 * nfb, slim_as);
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int tok = tt * 16 + l16;
-        if (tt >= ntt || tok >= cur.nvalid) continue;
+      for (int tt = 0; tt < kTT; ++tt) {
+        const int tok = (th * kTT + tt) * 16 + l16;
         const float am = fmaxf(fmaxf(s_amax[tok], s_amax[kTM + tok]), fmaxf(s_amax[2 * kTM + tok], s_amax[3 * kTM + tok]));
         const int e = scale_exp(am);
-        uint8_t* ap = aq + (size_t)(cur.r0 + tok) * F + f0 + 4 * g;
-        *reinterpret_cast<uint32_t*>(ap) = pack4_fp8(ldexpf(acc[0][tt][0], -e), ldexpf(acc[0][tt][1], -e),
-                                                     ldexpf(acc[0][tt][2], -e), ldexpf(acc[0][tt][3], -e));
-        *reinterpret_cast<uint32_t*>(ap + 16) = pack4_fp8(ldexpf(acc[1][tt][0], -e), ldexpf(acc[1][tt][1], -e),
-                                                          ldexpf(acc[1][tt][2], -e), ldexpf(acc[1][tt][3], -e));
-        if (wave == 0 && g == 0) as_[(size_t)(cur.r0 + tok) * nfb + cur.wb] = (uint8_t)(e + 127);
+        const uint32_t ao = (uint32_t)tok * (uint32_t)F + (uint32_t)(f0 + 4 * g);
+        __builtin_amdgcn_raw_buffer_store_b32(pack4_fp8(ldexpf(acc[0][tt][0], -e), ldexpf(acc[0][tt][1], -e),
+                                                        ldexpf(acc[0][tt][2], -e), ldexpf(acc[0][tt][3], -e)),
+                                              Ar, ao, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(pack4_fp8(ldexpf(acc[1][tt][0], -e), ldexpf(acc[1][tt][1], -e),
+                                                        ldexpf(acc[1][tt][2], -e), ldexpf(acc[1][tt][3], -e)),
+                                              Ar, ao + 16, 0, 0);
+        const uint32_t so = (wq == 0 && g == 0) ? (uint32_t)tok * (uint32_t)nfb + (uint32_t)cur.wb : slim_as;
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(e + 127), Sr, so, 0, 0);
       }
-    } else if (cur.wlive) {
-      const int h0 = cur.wb * kTN + wave * 64;
+    } else {
+      // the previous item's tiles not stored by this item's stages (fewer
+      // than 4 kTT stages), then this item's results take their place
+      for (int q = nst4; q < 4 * kTT; ++q) ystore_rt(q);
+      const int h0 = cur.wb * kTN + wq * 64;
+      // waves without weight tiles (a partial last block of H) store nothing: zero-sized buffer
+      Yp = make_rsrc(y + (size_t)cur.r0 * H, cur.wlive ? (uint32_t)cur.nvalid * (uint32_t)H * 4u : 0u);
+      yp_lane = ((uint32_t)(th * kTT * 16 + l16) * (uint32_t)H + (uint32_t)(cur.wlive ? h0 + 4 * g : 0)) * 4u;
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int tok = tt * 16 + l16;
-        if (tt >= ntt || tok >= cur.nvalid) continue;
-        float* yr = y + (size_t)(cur.r0 + tok) * H + h0 + 4 * g;
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          *reinterpret_cast<float4*>(yr + 16 * rt) =
-              make_float4(acc[rt][tt][0], acc[rt][tt][1], acc[rt][tt][2], acc[rt][tt][3]);
-      }
+        for (int tt = 0; tt < kTT; ++tt) yst[rt][tt] = acc[rt][tt];
     }
+    after_epi = true;
     // item boundary: every wave is done with this item's token scales and
     // amax; the next item's scales go in (visible after the next stage barrier)
     bare_barrier();
@@ -468,6 +545,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped(const uint8_t* __restrict__ 
     cur = nxt;
     gpar = (gpar + ngrp) & 1;
   }
+  if constexpr (!G1)
+    for (int q = 0; q < 4 * kTT; ++q) ystore_rt(q);  // the last item's results
 }
 
 static int num_cus() {
@@ -490,23 +569,29 @@ bool tiled_fits(int H, int F, int P_local) {
   return H / 128 <= kMaxStages && F / 128 <= kMaxStages && kTiledStaticLds + tiled_lds(P_local) <= kTiledLdsMax;
 }
 
+// Dynamic LDS above the default limit is opted into per kernel and device,
+// once per size.
+static hipError_t grant_lds(const void* fn, size_t lds, size_t (&granted)[64]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || lds > granted[dev]) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) granted[dev] = lds;
+  }
+  return hipSuccess;
+}
+
 template <bool G1>
 static hipError_t launch_grouped(const uint8_t* x, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw,
                                  const uint8_t* pws, uint8_t* aq, uint8_t* as, float* y, int H, int F, int P_local,
                                  hipStream_t st) {
   const size_t lds = tiled_lds(P_local);
-  // dynamic LDS above the default limit is opted into per device, once per size
   static size_t granted[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_grouped<G1>), lds, granted);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || lds > granted[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped<G1>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) granted[dev] = lds;
-  }
-  k_grouped<G1><<<num_cus() / 8 * 8, 256, lds, st>>>(x, xs, offsets, P_local, pw, pws, aq, as, y, H, F);
+  k_grouped<G1><<<num_cus() / 8 * 8, kNW * 64, lds, st>>>(x, xs, offsets, P_local, pw, pws, aq, as, y, H, F);
   return hipGetLastError();
 }
 

@@ -58,7 +58,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (each within
+// about one ulp): a few ulps overall, far inside the accumulation error of the
+// GEMM that produced g.  Very negative g: e^-g overflows to inf, 1/inf = 0.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
 
 // Block index -> work item such that consecutive items land on the same XCD.
 // The hardware deals workgroups round-robin over the 8 XCDs (block b runs on
