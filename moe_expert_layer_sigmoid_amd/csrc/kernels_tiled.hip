@@ -5,28 +5,28 @@
 // steps of at least 1024 tokens per rank [sglang PR 47065 "Use the aiter
 // MegaMoE small- and large-input paths", Modifications].
 //
-// Work item = (local slot s, weight block of 256 rows, token block of 128
-// rows of the slot's bucket), token block fastest, so the items that run at
-// the same time on one XCD share their weight block in that XCD's L2.  The
-// grid is one block per CU; each block walks items of its XCD's contiguous
-// range.
-//
-// Block = kNW waves, one block per CU.  The block tile is 128 tokens x 256
-// weight rows; weight quarter wq = wave % 4 (GEMM1: the gate and up tiles of
-// 32 columns of F; GEMM2: 64 rows of H, four 16-row tiles) runs on SIMD wq,
-// and with kNW = 8 two waves share each SIMD, one per half of the block's
-// eight 16-token tiles, so that one wave's LDS and barrier waits are filled
-// by the other's MFMAs.  K advances 128 per stage (one
-// V_MFMA_SCALE_F32_16X16X128_F8F6F4 per tile pair).
-//  - Token rows: direct-to-LDS DMA (buffer_load_dwordx4 ... lds), a ring of
-//    kRing stages issued kRing - 1 stages ahead; each stage row of 128 bytes
-//    is stored with its eight 16-byte pieces XOR-swizzled so the B-operand
-//    reads of a 16-token tile hit distinct banks.
-//  - Weight tiles (the packed layout is the MFMA operand order) and their
-//    scales: direct-to-LDS DMA into the same ring, read back with one
-//    ds_read_b128 per tile.
+// Both kernels are persistent: one block per CU walks the work items of its
+// XCD's contiguous range (block b runs on XCD b % 8), token block fastest, so
+// the items that run at the same time on one XCD share their weight block in
+// that XCD's L2.  K advances 128 per stage (one V_MFMA_SCALE_F32_16X16X128_
+// F8F6F4 per tile pair); two waves share each SIMD, so that one wave's LDS
+// and barrier waits are filled by the other's MFMAs.
+//  - Token rows and weight tiles: direct-to-LDS DMA (buffer_load_dwordx4 ...
+//    lds) into a ring of stages issued ahead of use; each token row of 128
+//    bytes is stored with its eight 16-byte pieces permuted so that the
+//    B-operand reads of a 16-token tile hit distinct banks; a weight tile
+//    (the packed layout is the MFMA operand order) is read back with one
+//    ds_read_b128 per lane.
 //  - Stage barriers are bare s_barrier with explicit vmcnt waits: the
 //    generic workgroup barrier would drain every load in flight.
+//  - k_gemm2_tiled (a6): items of 128 tokens x 256 rows of H; wave (wq, th)
+//    owns rows 64 wq .. + 63 against the token tiles of half th; a ring of
+//    four stages, three in flight; weight scales by DMA too; y tiles of an
+//    item written during the next item's stages.
+//  - k_gemm1_w (a5): items of 128 tokens x 512 weight rows (the gate and up
+//    rows of 256 columns of F); wave w owns 32 columns against all eight
+//    token tiles; a ring of three stages, two in flight; weight scales in
+//    registers; SwiGLU + fp8 requant epilogue.
 
 #include <type_traits>
 
@@ -53,20 +53,11 @@ constexpr int kSI = 2 / kWPS;      // scale DMA instructions per wave per scale 
 
 // vmcnt accounting.  A stage's DMA is waited for at the start of the stage
 // three later; after it the wave has issued two more stages of DMA (kXI +
-// kWI each) and, with kStageStores = 1 (GEMM2), one store per stage: three.
-// Scale-group DMA and token-scale loads only add to the count, which keeps
-// the wait sufficient.  (Scale groups are issued at least three stages
-// before their first use, with three stages of DMA after them by then.)
-template <bool G1>
-constexpr int kStageStores = G1 ? 0 : 1;
-template <bool G1>
-constexpr int kVmWait = 2 * (kXI + kWI) + 3 * kStageStores<G1>;
-// GEMM1's epilogue stores are issued after the DMA of the next item's first
-// three stages and, like them, count in vmcnt: every wave issues exactly
-// kEpiStores of them (rows past the item store out of the buffer's range,
-// which the hardware drops), so the waits of those three stages allow that
-// many more and never drain them.
-constexpr int kEpiStores = 3 * kTT;
+// kWI each) and one y store per stage: three.  Scale-group DMA and
+// token-scale loads only add to the count, which keeps the wait sufficient.
+// (Scale groups are issued at least three stages before their first use,
+// with three stages of DMA after them by then.)
+constexpr int kVmWait = 2 * (kXI + kWI) + 3;
 
 // Physical 16-byte piece of logical piece p in the stage row of the token at
 // position r (mod 16) of its tile: p ^ swz(r).  Measured on gfx950 for the
@@ -129,12 +120,13 @@ struct TItem {
   int tl[2];     // the wave's weight tiles: tl[0], tl[0] + 1, tl[1], tl[1] + 1
 };
 
-template <bool G1>
-__global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
-                                                    const int32_t* __restrict__ offsets, int P_local,
-                                                    const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws,
-                                                    uint8_t* __restrict__ aq, uint8_t* __restrict__ as_,
-                                                    float* __restrict__ y, int H, int F) {
+// GEMM2 (a6): y rows [bucket rows, H] f32 from the requantised act rows.
+__global__ __launch_bounds__(kNW * 64, 1) void k_gemm2_tiled(const uint8_t* __restrict__ xq,
+                                                             const uint8_t* __restrict__ xs,
+                                                             const int32_t* __restrict__ offsets, int P_local,
+                                                             const uint8_t* __restrict__ pw,
+                                                             const uint8_t* __restrict__ pws, float* __restrict__ y,
+                                                             int H, int F) {
   // DMA rings: one LDS object per ring slot, so that the compiler's LDS-DMA
   // tracking sees that the slot a stage reads is not the one just refilled
   // slot: kTM token rows x 128 B (swizzled), then 16 weight tiles x 1 KB
@@ -145,16 +137,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restri
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* const xring[kRing] = {r0s, r1s, r2s, r3s};
   uint8_t* const wring[kRing] = {r0s + kStage, r1s + kStage, r2s + kStage, r3s + kStage};
-  const int K = G1 ? H : F;
-  const int R = G1 ? 2 * F : H;
-  const int nwb = G1 ? F / kActBlock : (H + kTN - 1) / kTN;
+  const int K = F, R = H;
+  const int nwb = (H + kTN - 1) / kTN;
   const int nst = K / 128;               // stages with data (K is a multiple of 128)
   const int nst4 = (nst + 3) & ~3;       // stages run per item: whole ring turns
   const PackGeom Gm = pack_geom((uint32_t)R, (uint32_t)K);
   const int ngrp = (int)Gm.steps / 4;    // scale groups (8 stages each); 8 ngrp >= nst4
-  float* s_amax = reinterpret_cast<float*>(lds);            // [4 weight quarters][kTM]
-  int* s_pre = reinterpret_cast<int*>(s_amax + 4 * kTM);    // [P_local + 1] items before slot
-  int* s_off = s_pre + P_local + 1;                         // [P_local + 1] bucket offsets
+  int* s_pre = reinterpret_cast<int*>(lds);  // [P_local + 1] items before slot
+  int* s_off = s_pre + P_local + 1;           // [P_local + 1] bucket offsets
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave & 3, th = kWPS == 1 ? 0 : wave >> 2;  // weight quarter (SIMD), token group
@@ -217,16 +207,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restri
     it.r0 = __builtin_amdgcn_readfirstlane(s_off[s] + tb * kTM);
     it.nvalid = __builtin_amdgcn_readfirstlane(it.live ? min(kTM, n - tb * kTM) : 0);
     it.live = __builtin_amdgcn_readfirstlane(it.live);
-    it.wlive = it.live && (G1 || wb * kTN + wq * 64 < H);  // H is a multiple of 128
-    if (G1) {  // gate and up tiles of columns f0 .. f0 + 31
-      const int f0 = it.wb * kActBlock + wq * 32;
-      it.tl[0] = f0 / 16;
-      it.tl[1] = (F + f0) / 16;
-    } else {   // rows h0 .. h0 + 63
-      const int h0 = it.wb * kTN + wq * 64;
-      it.tl[0] = h0 / 16;
-      it.tl[1] = h0 / 16 + 2;
-    }
+    it.wlive = it.live && wb * kTN + wq * 64 < H;  // H is a multiple of 128
+    const int h0 = it.wb * kTN + wq * 64;         // rows h0 .. h0 + 63
+    it.tl[0] = h0 / 16;
+    it.tl[1] = h0 / 16 + 2;
     return it;
   };
 
@@ -407,7 +391,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restri
 
   // ---- first item: its token scales, first scale group and first stages
   TItem cur = decode(i0 + lb);
-  bool after_epi = false;  // GEMM1: an epilogue's stores are in flight (every item but the first)
   int gpar = 0;  // scale slot of the current item's group 0
   {
     uint32_t v[kXsPer];
@@ -420,7 +403,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restri
   for (int q = 0; q < kAhead; ++q) {
     dma_x(cur, xring[q], q);
     dma_w(cur, wring[q], q);
-    if constexpr (!G1) ystore(std::integral_constant<int, 0>{}, 4 * kTT);  // nothing yet: the per-stage count
+    ystore(std::integral_constant<int, 0>{}, 4 * kTT);  // nothing yet: the per-stage count
   }
 
   for (int item = i0 + lb; item < i1; item += nper) {
@@ -440,10 +423,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restri
     // this item or, past its end, of the next), compute stage q
     auto stage = [&](auto uc, int q) {
       constexpr int u = decltype(uc)::value;
-      if (G1 && after_epi && q < 3)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kVmWait<G1> + kEpiStores) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kVmWait<G1>) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kVmWait) : "memory");
       bare_barrier();
       if ((q & 7) == 0 && cur.wlive) {  // a new scale group (its DMA was issued at least three stages ago)
         const uint8_t* sp = sring + ((gpar + (q >> 3)) & 1) * kSGroup + wq * 2048 + lane * 8;
@@ -461,7 +441,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restri
         dma_x(nxt, xring[(u + kAhead) % kRing], q + kAhead - nst4);
         dma_w(nxt, wring[(u + kAhead) % kRing], q + kAhead - nst4);
       }
-      if constexpr (!G1) ystore(std::integral_constant<int, u>{}, q);  // q % 4 == u: stage loops start at multiples of 4
+      ystore(std::integral_constant<int, u>{}, q);  // q % 4 == u: stage loops start at multiples of 4
       compute(cur.wlive, xring[u], wring[u], q);
     };
     for (int q0 = 0; q0 < nst4 - 4; q0 += 4) {
@@ -480,73 +460,380 @@ __global__ __launch_bounds__(kNW * 64, 1) void k_grouped(const uint8_t* __restri
     stage(std::integral_constant<int, 2>{}, nst4 - 2);
     stage(std::integral_constant<int, 3>{}, nst4 - 1);
 
-    // ---- epilogue (LDS exchanges use bare barriers: the next item's DMA
-    // stays in flight)
-    if (G1) {
-      // SwiGLU in place: acc[0] / acc[1] become act of the gate tiles' columns
+    // ---- epilogue: the previous item's tiles not stored by this item's
+    // stages (fewer than 4 kTT stages), then this item's results take their
+    // place
+    for (int q = nst4; q < 4 * kTT; ++q) ystore_rt(q);
+    const int h0 = cur.wb * kTN + wq * 64;
+    // waves without weight tiles (a partial last block of H) store nothing: zero-sized buffer
+    Yp = make_rsrc(y + (size_t)cur.r0 * H, cur.wlive ? (uint32_t)cur.nvalid * (uint32_t)H * 4u : 0u);
+    yp_lane = ((uint32_t)(th * kTT * 16 + l16) * (uint32_t)H + (uint32_t)(cur.wlive ? h0 + 4 * g : 0)) * 4u;
 #pragma unroll
-      for (int tt = 0; tt < kTT; ++tt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[0][tt][r] = silu(acc[0][tt][r]) * acc[2][tt][r];
-          acc[1][tt][r] = silu(acc[1][tt][r]) * acc[3][tt][r];
-        }
-#pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
-        float m = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m = fmaxf(m, fmaxf(fabsf(acc[0][tt][r]), fabsf(acc[1][tt][r])));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        if (g == 0) s_amax[wq * kTM + (th * kTT + tt) * 16 + l16] = m;
-      }
-      MOE_LGKM_WAIT(0);
-      bare_barrier();
-      // stores through buffers sized to the item's rows: lanes past them are dropped
-      const int nfb = F / kActBlock;
-      const int f0 = cur.wb * kActBlock + wq * 32;
-      const rsrc_t Ar = make_rsrc(aq + (size_t)cur.r0 * F, (uint32_t)cur.nvalid * (uint32_t)F);
-      const uint32_t slim_as = (uint32_t)cur.nvalid * (uint32_t)nfb;
-      const rsrc_t Sr = make_rsrc(as_ + (size_t)cur.r0 * nfb, slim_as);
-#pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
-        const int tok = (th * kTT + tt) * 16 + l16;
-        const float am = fmaxf(fmaxf(s_amax[tok], s_amax[kTM + tok]), fmaxf(s_amax[2 * kTM + tok], s_amax[3 * kTM + tok]));
-        const int e = scale_exp(am);
-        const uint32_t ao = (uint32_t)tok * (uint32_t)F + (uint32_t)(f0 + 4 * g);
-        __builtin_amdgcn_raw_buffer_store_b32(pack4_fp8(ldexpf(acc[0][tt][0], -e), ldexpf(acc[0][tt][1], -e),
-                                                        ldexpf(acc[0][tt][2], -e), ldexpf(acc[0][tt][3], -e)),
-                                              Ar, ao, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(pack4_fp8(ldexpf(acc[1][tt][0], -e), ldexpf(acc[1][tt][1], -e),
-                                                        ldexpf(acc[1][tt][2], -e), ldexpf(acc[1][tt][3], -e)),
-                                              Ar, ao + 16, 0, 0);
-        const uint32_t so = (wq == 0 && g == 0) ? (uint32_t)tok * (uint32_t)nfb + (uint32_t)cur.wb : slim_as;
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(e + 127), Sr, so, 0, 0);
-      }
-    } else {
-      // the previous item's tiles not stored by this item's stages (fewer
-      // than 4 kTT stages), then this item's results take their place
-      for (int q = nst4; q < 4 * kTT; ++q) ystore_rt(q);
-      const int h0 = cur.wb * kTN + wq * 64;
-      // waves without weight tiles (a partial last block of H) store nothing: zero-sized buffer
-      Yp = make_rsrc(y + (size_t)cur.r0 * H, cur.wlive ? (uint32_t)cur.nvalid * (uint32_t)H * 4u : 0u);
-      yp_lane = ((uint32_t)(th * kTT * 16 + l16) * (uint32_t)H + (uint32_t)(cur.wlive ? h0 + 4 * g : 0)) * 4u;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) yst[rt][tt] = acc[rt][tt];
-    }
-    after_epi = true;
-    // item boundary: every wave is done with this item's token scales and
-    // amax; the next item's scales go in (visible after the next stage barrier)
+      for (int tt = 0; tt < kTT; ++tt) yst[rt][tt] = acc[rt][tt];
+    // item boundary: every wave is done with this item's token scales; the
+    // next item's go in (visible after the next stage barrier)
     bare_barrier();
     xs_store(nxt, xsn);
     MOE_LGKM_WAIT(0);
     cur = nxt;
     gpar = (gpar + ngrp) & 1;
   }
-  if constexpr (!G1)
-    for (int q = 0; q < 4 * kTT; ++q) ystore_rt(q);  // the last item's results
+  for (int q = 0; q < 4 * kTT; ++q) ystore_rt(q);  // the last item's results
+}
+
+// ---------------------------------------------------------------------------
+// GEMM1 (a5) on 128-token x 512-row tiles.  Eight waves, two per SIMD; wave
+// w owns the gate and up tiles of 32 columns of F (four 16-row weight tiles)
+// against all eight 16-token tiles: 32 accumulators (128 registers).  A
+// stage of 128 K is 32 MFMAs per wave over 48 KB of DMA per block (16 KB
+// tokens + 32 KB weights): twice the MFMA work per stage barrier and per
+// byte moved of the 128 x 256 tile, and fewer LDS reads per MFMA.  Weight
+// scales come into registers (four 8-byte loads per wave per eight stages,
+// issued seven stages ahead); the ring holds three stages, two in flight.
+// Work item = (slot, block of 256 columns of F, token block of 128 rows).
+// ---------------------------------------------------------------------------
+constexpr int kG1W = 8;                    // waves
+constexpr int kG1Ring = 3;                 // ring stages
+constexpr int kG1Ahead = kG1Ring - 1;      // stages in flight ahead of use
+constexpr int kG1WStage = 32 * 1024;       // weight bytes per stage (32 tiles x 1 KB)
+constexpr int kG1Cols = 256;               // act columns per item (512 weight rows)
+constexpr int kG1XI = kStage / 1024 / kG1W;  // token DMA instructions per wave per stage (2)
+constexpr int kG1WI = 4;                   // weight DMA instructions per wave per stage
+// A stage's DMA is waited for at the start of the stage two later, with one
+// more stage of DMA issued after it; the epilogue's stores (3 per token tile)
+// follow the DMA of the next item's first two stages.
+constexpr int kG1Vm = kG1XI + kG1WI;
+constexpr int kG1Epi = 3 * 8;
+constexpr size_t kG1StaticLds = (size_t)kG1Ring * (kStage + kG1WStage) + kTM * kMaxStages;
+static size_t g1w_lds(int P_local) { return kG1W * kTM * sizeof(float) + 2 * (size_t)(P_local + 1) * sizeof(int); }
+
+__global__ __launch_bounds__(kG1W * 64, 1) void k_gemm1_w(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                                          const int32_t* __restrict__ offsets, int P_local,
+                                                          const uint8_t* __restrict__ pw,
+                                                          const uint8_t* __restrict__ pws, uint8_t* __restrict__ aq,
+                                                          uint8_t* __restrict__ as_, int H, int F) {
+  __shared__ __align__(16) uint8_t g0s[kStage + kG1WStage], g1s[kStage + kG1WStage], g2s[kStage + kG1WStage];
+  __shared__ __align__(16) uint8_t s_xs[kTM * kMaxStages];  // [stage][16][8] token scales
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int K = H, R = 2 * F;
+  const int nwb = (F + kG1Cols - 1) / kG1Cols;
+  const int nst = K / 128;
+  const int nst4 = (nst + 3) & ~3;
+  const PackGeom Gm = pack_geom((uint32_t)R, (uint32_t)K);
+  const int ngrp = (int)Gm.steps / 4;  // scale words of 8 stages
+  float* s_amax = reinterpret_cast<float*>(lds);            // [8 waves][kTM]
+  int* s_pre = reinterpret_cast<int*>(s_amax + kG1W * kTM);  // [P_local + 1] items before slot
+  int* s_off = s_pre + P_local + 1;                         // [P_local + 1] bucket offsets
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int sw = swz(l16);
+
+  for (int p = tid; p <= P_local; p += blockDim.x) s_off[p] = offsets[p];
+  __syncthreads();
+  for (int p = tid; p < P_local; p += blockDim.x) s_pre[p + 1] = (s_off[p + 1] - s_off[p] + kTM - 1) / kTM * nwb;
+  if (tid == 0) s_pre[0] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int p = 1; p <= P_local; ++p) {
+      run += s_pre[p];
+      s_pre[p] = run;
+    }
+  }
+  __syncthreads();
+  const int nitems = s_pre[P_local];
+  const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, lb = blockIdx.x >> 3;
+  const int chunk = (nitems + 7) / 8;
+  const int i0 = xcd * chunk, i1 = min(nitems, i0 + chunk);
+  if (i0 + lb >= i1) return;  // block-uniform: no item for this block
+
+  uint32_t xt[kG1XI], xp[kG1XI];  // token DMA instruction wave + 8m: token row, byte offset of the lane's piece
+#pragma unroll
+  for (int m = 0; m < kG1XI; ++m) {
+    const int t = 8 * (wave + kG1W * m) + (lane >> 3);
+    xt[m] = (uint32_t)t;
+    xp[m] = 16u * (uint32_t)((lane & 7) ^ swz(t & 15));
+  }
+  const uint32_t wlane = 16u * lane, slane = 8u * lane;
+  const uint32_t wlim = (uint32_t)Gm.data_slot, slim = (uint32_t)Gm.scale_slot;
+
+  auto decode = [&](int item) {
+    TItem it;
+    it.live = item < i1;
+    int s = 0, wb = 0, tb = 0, n = 0;
+    if (it.live) {
+      int lo = 0, hi = P_local - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= item) lo = mid;
+        else hi = mid - 1;
+      }
+      s = lo;
+      n = s_off[s + 1] - s_off[s];
+      const int ntb = (n + kTM - 1) / kTM;
+      const int local = item - s_pre[s];
+      wb = local / ntb;
+      tb = local - wb * ntb;
+    }
+    it.s = __builtin_amdgcn_readfirstlane(s);
+    it.wb = __builtin_amdgcn_readfirstlane(wb);
+    it.r0 = __builtin_amdgcn_readfirstlane(s_off[s] + tb * kTM);
+    it.nvalid = __builtin_amdgcn_readfirstlane(it.live ? min(kTM, n - tb * kTM) : 0);
+    it.live = __builtin_amdgcn_readfirstlane(it.live);
+    const int c0 = it.wb * kG1Cols + wave * 32;  // this wave's 32 columns of F
+    it.wlive = it.live && c0 < F;               // F is a multiple of 128
+    it.tl[0] = c0 / 16;                          // gate tiles tl[0], tl[0] + 1
+    it.tl[1] = (F + c0) / 16;                    // up tiles tl[1], tl[1] + 1
+    return it;
+  };
+
+  auto dma_x = [&](const TItem it, uint8_t* slot, int q) {  // token stage q
+    const bool live = it.live && q < nst;
+    const uint32_t xlim = (uint32_t)it.nvalid * (uint32_t)K;
+    const rsrc_t Xr = make_rsrc(xq + (size_t)it.r0 * K, xlim);
+#pragma unroll
+    for (int m = 0; m < kG1XI; ++m) {
+      const uint32_t vo = (live && xt[m] < (uint32_t)it.nvalid) ? xt[m] * (uint32_t)K + xp[m] : xlim;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (lds_ptr_t)(slot + (wave + kG1W * m) * 1024), 16, vo,
+                                               live ? (uint32_t)q * 128u : 0u, 0, 0);
+    }
+  };
+  // Loads of nothing (no item, no tiles, past K) go through a zero-sized
+  // buffer, so the lane offsets stay loop constants.
+  auto dma_w = [&](const TItem it, uint8_t* slot, int q) {  // this wave's four weight tiles of stage q
+    const bool live = it.wlive && q < nst;
+    const rsrc_t Wr = make_rsrc(pw + (size_t)it.s * Gm.data_slot, live ? wlim : 0u);
+    const uint32_t so = (uint32_t)(q >> 1) * 2048u + (uint32_t)(q & 1) * 1024u;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const uint32_t tile = (uint32_t)(((a >> 1) ? it.tl[1] : it.tl[0]) + (a & 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Wr, (lds_ptr_t)(slot + wave * 4096 + a * 1024), 16, wlane,
+                                               live ? tile * (uint32_t)Gm.data_tile + so : 0u, 0, kWeightNt);
+    }
+  };
+  // the four tiles' scales of group grp (stages 8 grp .. 8 grp + 7): byte q % 8 scales stage q
+  auto load_scales = [&](const TItem it, int grp, v2i (&sc)[4]) {
+    const bool live = it.wlive && grp < ngrp;
+    const rsrc_t Sr = make_rsrc(pws + (size_t)it.s * Gm.scale_slot, live ? slim : 0u);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const uint32_t tile = (uint32_t)(((a >> 1) ? it.tl[1] : it.tl[0]) + (a & 1));
+      sc[a] = buf_load8(Sr, slane, live ? tile * (uint32_t)Gm.scale_tile + (uint32_t)grp * 512u : 0u);
+    }
+  };
+
+  constexpr int kTPR = kG1W * 64 / kTM;          // threads per token row
+  constexpr int kXsPer = kMaxStages / 4 / kTPR;  // dwords per thread
+  const bool xs_dw = (nst & 3) == 0;
+  auto xs_fetch = [&](const TItem it, uint32_t (&v)[kXsPer]) {
+    const int t = tid / kTPR;
+    const bool ok = xs_dw && it.live && t < it.nvalid;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(xs + (size_t)(it.r0 + t) * nst);
+#pragma unroll
+    for (int j = 0; j < kXsPer; ++j) {
+      const int d = (tid % kTPR) + kTPR * j;
+      v[j] = (ok && 4 * d < nst) ? __hip_atomic_load(src + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
+    }
+  };
+  auto xs_store = [&](const TItem it, const uint32_t (&v)[kXsPer]) {
+    const int t = tid / kTPR;
+    uint8_t* dst = s_xs + (t & 15) * 8 + (t >> 4);
+    if (xs_dw) {
+#pragma unroll
+      for (int j = 0; j < kXsPer; ++j) {
+        const int d = (tid % kTPR) + kTPR * j;
+        if (4 * d < nst4) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) dst[(4 * d + bb) * kTM] = (uint8_t)(v[j] >> (8 * bb));
+        }
+      }
+    } else {
+      const bool ok = it.live && t < it.nvalid;
+      const uint8_t* src = xs + (size_t)(it.r0 + t) * nst;
+      for (int c = tid % kTPR; c < nst4; c += kTPR) dst[c * kTM] = (ok && c < nst) ? src[c] : (uint8_t)0;
+    }
+  };
+
+  const int o_lo = (g ^ sw) * 16, o_hi = ((g + 4) ^ sw) * 16;
+  v2i scc[4], scn[4];  // weight scales: the current group, the next one
+  v4f acc[4][8];
+  constexpr int kTile = 16 * 128;
+
+  auto ldb = [&](V8T& b, uint32_t blo, uint32_t bhi, auto ttc) {
+    constexpr int o = decltype(ttc)::value * kTile;
+    b.h[0] = lds_read16_at<o>(blo);
+    b.h[1] = lds_read16_at<o>(bhi);
+  };
+  // stage q: LDS reads in issue order (they complete in order): weights (4),
+  // token scales (1), token tiles 0 and 1 (2 + 2), then tile tt + 2's two
+  // reads before tile tt's four MFMAs.
+  auto compute = [&](bool wlive, const uint8_t* xs_slot, const uint8_t* w_slot, int q) {
+    if (!wlive) return;
+    const uint32_t aa = lds_addr(w_slot + wave * 4096 + lane * 16);
+    const uint32_t blo = lds_addr(xs_slot + l16 * 128 + o_lo), bhi = lds_addr(xs_slot + l16 * 128 + o_hi);
+    v4i a[4];
+    a[0] = lds_read16_at<0>(aa);
+    a[1] = lds_read16_at<1024>(aa);
+    a[2] = lds_read16_at<2048>(aa);
+    a[3] = lds_read16_at<3072>(aa);
+    const v2i sbw = lds_read8(s_xs + q * kTM + l16 * 8);
+    V8T b[3];
+    ldb(b[0], blo, bhi, std::integral_constant<int, 0>{});
+    ldb(b[1], blo, bhi, std::integral_constant<int, 1>{});
+    int sa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = (int)((uint32_t)((q & 4) ? scc[i].y : scc[i].x) >> (8 * (q & 3)));
+    MOE_LGKM_WAIT(4);  // weights and token scales are in
+    __builtin_amdgcn_sched_barrier(0);
+    int sb[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) sb[tt] = (int)(((uint32_t)(tt < 4 ? sbw.x : sbw.y) >> (8 * (tt & 3))) & 0xFFu);
+    __builtin_amdgcn_sched_barrier(0);
+    auto tile = [&](auto ttc) {
+      constexpr int tt = decltype(ttc)::value;
+      if constexpr (tt + 2 < 8) ldb(b[(tt + 2) % 3], blo, bhi, std::integral_constant<int, tt + 2>{});
+      if constexpr (tt + 2 < 8) MOE_LGKM_WAIT(4);
+      else if constexpr (tt + 1 < 8) MOE_LGKM_WAIT(2);
+      else MOE_LGKM_WAIT(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][tt] = mfma_fp4_fp8<0>(a[i], b[tt % 3].v, acc[i][tt], sa[i], sb[tt]);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    tile(std::integral_constant<int, 0>{});
+    tile(std::integral_constant<int, 1>{});
+    tile(std::integral_constant<int, 2>{});
+    tile(std::integral_constant<int, 3>{});
+    tile(std::integral_constant<int, 4>{});
+    tile(std::integral_constant<int, 5>{});
+    tile(std::integral_constant<int, 6>{});
+    tile(std::integral_constant<int, 7>{});
+  };
+
+  auto ring = [&](int i) -> uint8_t* { return i == 0 ? g0s : (i == 1 ? g1s : g2s); };  // a select: no table of LDS addresses
+
+  // ---- first item: its token scales, first scale group and first stages
+  TItem cur = decode(i0 + lb);
+  bool after_epi = false;  // an epilogue's stores are in flight (every item but the first)
+  {
+    uint32_t v[kXsPer];
+    xs_fetch(cur, v);
+    xs_store(cur, v);
+  }
+  load_scales(cur, 0, scn);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kG1Ahead; ++q) {
+    dma_x(cur, ring(q), q);
+    dma_w(cur, ring(q) + kStage, q);
+  }
+  int slot = 0;  // ring slot of the current stage
+
+  for (int item = i0 + lb; item < i1; item += nper) {
+    const TItem nxt = decode(item + nper);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) acc[i][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // one stage: wait for its DMA (own, then everyone's via the barrier,
+    // which also retires the slot the next DMA refills), issue stage q + 2
+    // (of this item or, past its end, of the next), compute stage q
+    auto stage = [&](int q) {
+      if (after_epi && q < kG1Ahead)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kG1Vm + kG1Epi) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kG1Vm) : "memory");
+      bare_barrier();
+      if ((q & 7) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) scc[i] = scn[i];
+      }
+      // the next scale group, of this item or the next item's first; issued
+      // before the stage's DMA, so that any wait the compiler places for it
+      // leaves that DMA in flight
+      if ((q & 7) == 1) {
+        if ((q >> 3) + 1 < ngrp && 8 * ((q >> 3) + 1) < nst4) load_scales(cur, (q >> 3) + 1, scn);
+        else load_scales(nxt, 0, scn);
+      }
+      uint8_t* const fill = ring(slot == 0 ? kG1Ring - 1 : slot - 1);  // the slot read by stage q - 1
+      if (q + kG1Ahead < nst4) {
+        dma_x(cur, fill, q + kG1Ahead);
+        dma_w(cur, fill + kStage, q + kG1Ahead);
+      } else {
+        dma_x(nxt, fill, q + kG1Ahead - nst4);
+        dma_w(nxt, fill + kStage, q + kG1Ahead - nst4);
+      }
+      compute(cur.wlive, ring(slot), ring(slot) + kStage, q);
+      slot = slot == kG1Ring - 1 ? 0 : slot + 1;
+    };
+    for (int q0 = 0; q0 < nst4 - 4; q0 += 4) {
+      stage(q0);
+      stage(q0 + 1);
+      stage(q0 + 2);
+      stage(q0 + 3);
+    }
+    uint32_t xsn[kXsPer];
+    xs_fetch(nxt, xsn);
+    stage(nst4 - 4);
+    stage(nst4 - 3);
+    stage(nst4 - 2);
+    stage(nst4 - 1);
+
+    // ---- epilogue: SwiGLU in place (acc[0..1] become act of the gate
+    // tiles' columns), the requant amax over 128 columns (this wave's 32 and
+    // the three other waves of its group of four), fp8 codes and scales
+    // through buffers sized to the item's rows
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[0][tt][r] = silu(acc[0][tt][r]) * acc[2][tt][r];
+        acc[1][tt][r] = silu(acc[1][tt][r]) * acc[3][tt][r];
+      }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, fmaxf(fabsf(acc[0][tt][r]), fabsf(acc[1][tt][r])));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (g == 0) s_amax[wave * kTM + tt * 16 + l16] = m;
+    }
+    MOE_LGKM_WAIT(0);
+    bare_barrier();
+    {
+      const int nfb = F / kActBlock;
+      const int c0 = cur.wb * kG1Cols + wave * 32;
+      const rsrc_t Ar = make_rsrc(aq + (size_t)cur.r0 * F, cur.wlive ? (uint32_t)cur.nvalid * (uint32_t)F : 0u);
+      const uint32_t slim_as = (uint32_t)cur.nvalid * (uint32_t)nfb;
+      const rsrc_t Sr = make_rsrc(as_ + (size_t)cur.r0 * nfb, cur.wlive ? slim_as : 0u);
+      const float* am0 = s_amax + (wave & ~3) * kTM;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int tok = tt * 16 + l16;
+        const int e = scale_exp(fmaxf(fmaxf(am0[tok], am0[kTM + tok]), fmaxf(am0[2 * kTM + tok], am0[3 * kTM + tok])));
+        const uint32_t ao = (uint32_t)tok * (uint32_t)F + (uint32_t)(c0 + 4 * g);
+        __builtin_amdgcn_raw_buffer_store_b32(pack4_fp8(ldexpf(acc[0][tt][0], -e), ldexpf(acc[0][tt][1], -e),
+                                                        ldexpf(acc[0][tt][2], -e), ldexpf(acc[0][tt][3], -e)),
+                                              Ar, ao, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(pack4_fp8(ldexpf(acc[1][tt][0], -e), ldexpf(acc[1][tt][1], -e),
+                                                        ldexpf(acc[1][tt][2], -e), ldexpf(acc[1][tt][3], -e)),
+                                              Ar, ao + 16u, 0, 0);
+        const uint32_t so = ((wave & 3) == 0 && g == 0) ? (uint32_t)tok * (uint32_t)nfb + (uint32_t)(c0 / kActBlock)
+                                                        : slim_as;
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(e + 127), Sr, so, 0, 0);
+      }
+    }
+    after_epi = true;
+    bare_barrier();  // every wave is done with this item's token scales and amax
+    xs_store(nxt, xsn);
+    MOE_LGKM_WAIT(0);
+    cur = nxt;
+  }
 }
 
 static int num_cus() {
@@ -562,11 +849,12 @@ static int num_cus() {
 
 constexpr size_t kTiledStaticLds = (size_t)kRing * (kStage + kWStage) + 2 * kSGroup + kTM * kMaxStages;
 
-// dynamic LDS: the requant amax, the item prefix and the bucket offsets
-static size_t tiled_lds(int P_local) { return 4 * kTM * sizeof(float) + 2 * (size_t)(P_local + 1) * sizeof(int); }
+// dynamic LDS of the GEMM2 kernel: the item prefix and the bucket offsets
+static size_t tiled_lds(int P_local) { return 2 * (size_t)(P_local + 1) * sizeof(int); }
 
 bool tiled_fits(int H, int F, int P_local) {
-  return H / 128 <= kMaxStages && F / 128 <= kMaxStages && kTiledStaticLds + tiled_lds(P_local) <= kTiledLdsMax;
+  return H / 128 <= kMaxStages && F / 128 <= kMaxStages && kTiledStaticLds + tiled_lds(P_local) <= kTiledLdsMax &&
+         kG1StaticLds + g1w_lds(P_local) <= kTiledLdsMax;
 }
 
 // Dynamic LDS above the default limit is opted into per kernel and device,
@@ -583,27 +871,25 @@ static hipError_t grant_lds(const void* fn, size_t lds, size_t (&granted)[64]) {
   return hipSuccess;
 }
 
-template <bool G1>
-static hipError_t launch_grouped(const uint8_t* x, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw,
-                                 const uint8_t* pws, uint8_t* aq, uint8_t* as, float* y, int H, int F, int P_local,
-                                 hipStream_t st) {
-  const size_t lds = tiled_lds(P_local);
-  static size_t granted[64] = {};
-  hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_grouped<G1>), lds, granted);
-  if (e != hipSuccess) return e;
-  k_grouped<G1><<<num_cus() / 8 * 8, kNW * 64, lds, st>>>(x, xs, offsets, P_local, pw, pws, aq, as, y, H, F);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
                               hipStream_t st) {
-  return launch_grouped<true>(xq, xs, offsets, pw1, pw1s, aq, as, nullptr, H, F, P_local, st);
+  const size_t lds = g1w_lds(P_local);
+  static size_t granted[64] = {};
+  hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_gemm1_w), lds, granted);
+  if (e != hipSuccess) return e;
+  k_gemm1_w<<<num_cus() / 8 * 8, kG1W * 64, lds, st>>>(xq, xs, offsets, P_local, pw1, pw1s, aq, as, H, F);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                               const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
-  return launch_grouped<false>(aq, as, offsets, pw2, pw2s, nullptr, nullptr, y, H, F, P_local, st);
+  const size_t lds = tiled_lds(P_local);
+  static size_t granted[64] = {};
+  hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_gemm2_tiled), lds, granted);
+  if (e != hipSuccess) return e;
+  k_gemm2_tiled<<<num_cus() / 8 * 8, kNW * 64, lds, st>>>(aq, as, offsets, P_local, pw2, pw2s, y, H, F);
+  return hipGetLastError();
 }
 
 }  // namespace moe
