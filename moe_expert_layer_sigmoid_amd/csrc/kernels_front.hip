@@ -297,21 +297,16 @@ hipError_t launch_scan(int nch, int P_total, int p0, int P_local, const int32_t*
 }
 
 // a4 arithmetic for one lane's 8 columns of a 128-column block (16 lanes per
-// block): e = smallest integer with amax <= 448 * 2^e over the block, codes
-// RNE e4m3fn(x * 2^-e).  `ok` false: the lane holds zeros (columns past H).
-__device__ __forceinline__ int quant8(const uint16_t* __restrict__ src, bool ok, uint2& q) {
+// block), on eight bf16 values already loaded (zeros for columns past H):
+// e = smallest integer with amax <= 448 * 2^e over the block, codes
+// RNE e4m3fn(x * 2^-e).
+__device__ __forceinline__ int quant8_raw(const uint4 raw, uint2& q) {
   float v[8];
-  if (ok) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(src);
-    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(wd[i] << 16);
-      v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(wd[i] << 16);
+    v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
   }
   float am = 0.0f;
 #pragma unroll
@@ -324,14 +319,23 @@ __device__ __forceinline__ int quant8(const uint16_t* __restrict__ src, bool ok,
   return e;
 }
 
+// The same, loading the lane's 8 columns (`ok` false: zeros).
+__device__ __forceinline__ int quant8(const uint16_t* __restrict__ src, bool ok, uint2& q) {
+  return quant8_raw(ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0), q);
+}
+
 // ---------------------------------------------------------------------------
-// a3 (part 3) + a4: one wavefront per (token, 512-column chunk).  Lanes j < k
-// resolve the row of pair (t, j) (base of its chunk and slot + rank; the
-// chunk-0 wave also writes the row maps), then the wave quantises its four
-// 128-column blocks: 16 lanes per block, 8 bf16 per lane; the block amax gives
+// a3 (part 3) + a4: one wavefront per (token, kQC 512-column chunks).  Lanes
+// j < k resolve the row of pair (t, j) (base of its chunk and slot + rank;
+// the wave of chunk 0 also writes the row maps); the wave then loads all its
+// columns at once (one 16-byte load per lane and chunk) and quantises each
+// 128-column block: 16 lanes per block, 8 bf16 per lane; the block amax gives
 // the e8m0 exponent, codes are RNE e4m3fn of x * 2^-e; the same bytes go to
-// every local row of the token.
+// every local row of the token.  Tokens without a local pair read nothing.
 // ---------------------------------------------------------------------------
+constexpr int kQC = 4;  // 512-column chunks per wavefront (quantise)
+constexpr int kCC = 4;  // 512-column chunks per wavefront (combine; 2 and 7 measured the same)
+
 __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16_t* __restrict__ x,
                                                const int32_t* __restrict__ phys, int p0, int P_local,
                                                const int32_t* __restrict__ base, const int32_t* __restrict__ rank,
@@ -339,9 +343,9 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
                                                int32_t* __restrict__ row_of_pair, int32_t* __restrict__ pair_of_row) {
   const int lane = threadIdx.x & 63;
   const int nb = H / kActBlock;
-  const int nc = (nb + 3) / 4;
+  const int ng = (H + 512 * kQC - 1) / (512 * kQC);
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t = wid / nc, ch = wid - t * nc;
+  const int t = wid / ng, grp = wid - t * ng;
   if (t >= T) return;  // wave-uniform
   int myrow = -1;
   if (lane < k) {
@@ -350,9 +354,9 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
     if (p >= p0 && p < p0 + P_local) {
       const int s = p - p0;
       myrow = base[(size_t)(t / kChunkTokens) * P_local + s] + rank[pr];
-      if (ch == 0) pair_of_row[myrow] = (int32_t)pr;
+      if (grp == 0) pair_of_row[myrow] = (int32_t)pr;
     }
-    if (ch == 0) row_of_pair[pr] = myrow;
+    if (grp == 0) row_of_pair[pr] = myrow;
   }
   int rows[16];
   bool any = false;
@@ -363,18 +367,28 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
     any |= rows[j] >= 0;
   }
   if (!any) return;
-  const int b = ch * 4 + (lane >> 4);
-  const bool ok = b < nb;
   const int sub = lane & 15;  // 8 columns each
-  uint2 q;
-  const int e = quant8(x + (size_t)t * H + b * kActBlock + sub * 8, ok, q);
-  if (ok) {
+  uint4 raw[kQC];
+  bool ok[kQC];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (rows[j] < 0) continue;  // wave-uniform
-      const size_t r = (size_t)rows[j];
-      *reinterpret_cast<uint2*>(xq + r * H + b * kActBlock + sub * 8) = q;
-      if (sub == 0) xs[r * nb + b] = (uint8_t)(e + 127);
+  for (int c = 0; c < kQC; ++c) {  // all loads first
+    const int b = (grp * kQC + c) * 4 + (lane >> 4);
+    ok[c] = b < nb;
+    raw[c] = ok[c] ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + b * kActBlock + sub * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < kQC; ++c) {
+    const int b = (grp * kQC + c) * 4 + (lane >> 4);
+    uint2 q;
+    const int e = quant8_raw(raw[c], q);
+    if (ok[c]) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (rows[j] < 0) continue;  // wave-uniform
+        const size_t r = (size_t)rows[j];
+        *reinterpret_cast<uint2*>(xq + r * H + b * kActBlock + sub * 8) = q;
+        if (sub == 0) xs[r * nb + b] = (uint8_t)(e + 127);
+      }
     }
   }
 }
@@ -383,25 +397,26 @@ hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* p
                         const int32_t* base, const int32_t* rank, uint8_t* xq, uint8_t* xs, int32_t* row_of_pair,
                         int32_t* pair_of_row, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const int nc = (H / kActBlock + 3) / 4;
-  const long waves = (long)T * nc;
+  const int ng = (H + 512 * kQC - 1) / (512 * kQC);
+  const long waves = (long)T * ng;
   k_quant<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, x, phys, p0, P_local, base, rank, xq, xs,
                                                        row_of_pair, pair_of_row);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// a7 combine: one wavefront per (token, 512-column chunk), 8 columns per lane;
-// out[t] = sum over local j ascending of w[t][j] * y[row(t, j)] (f32 fma
-// chain), rounded to bf16 (nearest even).
+// a7 combine: one wavefront per (token, kCC 512-column chunks), 8 columns per
+// lane and chunk; out[t] = sum over local j ascending of w[t][j] *
+// y[row(t, j)] (f32 fma chain), rounded to bf16 (nearest even).  A row's
+// loads for all the wave's chunks are issued together.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const float* __restrict__ y,
                                                  const int32_t* __restrict__ row_of_pair,
                                                  const float* __restrict__ w, uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int nc = (H + 511) / 512;
+  const int ng = (H + 512 * kCC - 1) / (512 * kCC);
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t = wid / nc, ch = wid - t * nc;
+  const int t = wid / ng, grp = wid - t * ng;
   if (t >= T) return;
   int myrow = -1;
   float myw = 0.0f;
@@ -417,38 +432,51 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
     ws[j] = __shfl(myw, j);
     rows[j] = j < k ? r : -1;
   }
-  const int h = ch * 512 + lane * 8;
-  if (h >= H) return;
-  float a[8];
+  float a[kCC][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+  for (int c = 0; c < kCC; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[c][i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (rows[j] < 0) continue;  // wave-uniform
-    const float* yr = y + (size_t)rows[j] * H + h;
-    const float4 y0 = *reinterpret_cast<const float4*>(yr);
-    const float4 y1 = *reinterpret_cast<const float4*>(yr + 4);
-    a[0] = fmaf(ws[j], y0.x, a[0]);
-    a[1] = fmaf(ws[j], y0.y, a[1]);
-    a[2] = fmaf(ws[j], y0.z, a[2]);
-    a[3] = fmaf(ws[j], y0.w, a[3]);
-    a[4] = fmaf(ws[j], y1.x, a[4]);
-    a[5] = fmaf(ws[j], y1.y, a[5]);
-    a[6] = fmaf(ws[j], y1.z, a[6]);
-    a[7] = fmaf(ws[j], y1.w, a[7]);
+    float4 v[kCC][2];
+#pragma unroll
+    for (int c = 0; c < kCC; ++c) {
+      const int h = (grp * kCC + c) * 512 + lane * 8;
+      const float* yr = y + (size_t)rows[j] * H + h;
+      v[c][0] = h < H ? *reinterpret_cast<const float4*>(yr) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[c][1] = h < H ? *reinterpret_cast<const float4*>(yr + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int c = 0; c < kCC; ++c) {
+      a[c][0] = fmaf(ws[j], v[c][0].x, a[c][0]);
+      a[c][1] = fmaf(ws[j], v[c][0].y, a[c][1]);
+      a[c][2] = fmaf(ws[j], v[c][0].z, a[c][2]);
+      a[c][3] = fmaf(ws[j], v[c][0].w, a[c][3]);
+      a[c][4] = fmaf(ws[j], v[c][1].x, a[c][4]);
+      a[c][5] = fmaf(ws[j], v[c][1].y, a[c][5]);
+      a[c][6] = fmaf(ws[j], v[c][1].z, a[c][6]);
+      a[c][7] = fmaf(ws[j], v[c][1].w, a[c][7]);
+    }
   }
-  uint4 o;
-  o.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
-  o.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
-  o.z = (uint32_t)f32_to_bf16(a[4]) | ((uint32_t)f32_to_bf16(a[5]) << 16);
-  o.w = (uint32_t)f32_to_bf16(a[6]) | ((uint32_t)f32_to_bf16(a[7]) << 16);
-  *reinterpret_cast<uint4*>(out + (size_t)t * H + h) = o;
+#pragma unroll
+  for (int c = 0; c < kCC; ++c) {
+    const int h = (grp * kCC + c) * 512 + lane * 8;
+    if (h >= H) continue;
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16(a[c][0]) | ((uint32_t)f32_to_bf16(a[c][1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(a[c][2]) | ((uint32_t)f32_to_bf16(a[c][3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(a[c][4]) | ((uint32_t)f32_to_bf16(a[c][5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(a[c][6]) | ((uint32_t)f32_to_bf16(a[c][7]) << 16);
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + h) = o;
+  }
 }
 
 hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* row_of_pair, const float* w,
                           uint16_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const long waves = (long)T * ((H + 511) / 512);
+  const long waves = (long)T * ((H + 512 * kCC - 1) / (512 * kCC));
   k_combine<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, y, row_of_pair, w, out);
   return hipGetLastError();
 }
