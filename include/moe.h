@@ -90,7 +90,8 @@ typedef enum {
                            pairs itself; combine + load record.  No bucket scan or permute.
                            T <= 1024 (else MOE_ERR_UNSUPPORTED). */
   MOE_PATH_STAGED = 2,  /* the component calls in sequence (bucketed rows, weight streaming) */
-  MOE_PATH_LARGE_M = 3  /* bucketed rows, persistent tiled GEMMs for many rows per expert */
+  MOE_PATH_LARGE_M = 3  /* bucketed rows, persistent tiled GEMMs once the mean rows per physical
+                           slot (T k / P_total) exceed 24, weight streaming below */
 } moe_path_t;
 
 /* Problem sizes of one call.  Limits: 0 <= T <= T_max <= 1<<20; H, F

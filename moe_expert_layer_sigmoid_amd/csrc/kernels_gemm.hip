@@ -97,26 +97,29 @@ __device__ __forceinline__ v4f mfma_ij(v4i a, v8i b, v4f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, kFmtFp4, kFmtFp8, IA, sa, IB, sb);
 }
 
-// One wave's operands: packed weight tiles (A) and one token tile (B).
+// One wave's operands: packed weight tiles (A) and NT token tiles (B) that
+// share each weight load.
+template <int NT>
 struct SOps {
-  rsrc_t w;            // packed data of the slot
-  rsrc_t ws;           // packed scales of the slot
-  rsrc_t x;            // the token tile's rows
-  uint32_t wt[4];      // tile * data_tile + 16 * lane
-  uint32_t wst[4];     // tile * scale_tile + 8 * lane
-  uint32_t xlo, xhi;   // token row * K + 16 g, + 64
-  const uint8_t* sxs;  // LDS: this lane's token's 128-column scales (zero-padded)
+  rsrc_t w;                // packed data of the slot
+  rsrc_t ws;               // packed scales of the slot
+  rsrc_t x;                // the token rows
+  uint32_t wt[4];          // tile * data_tile + 16 * lane
+  uint32_t wst[4];         // tile * scale_tile + 8 * lane
+  uint32_t xlo[NT];        // per token tile: token row * K + 16 g (past the buffer: zeros)
+  const uint8_t* sxs[NT];  // LDS: this lane's token's 128-column scales (zero-padded)
 };
 
+template <int NT>
 struct SStage {
   v4i a[4][2];
-  V8 b[2];
+  V8 b[NT][2];
 };
 
 // Operands of K step st; `gofs` moves the weight tiles to another group of
 // the wave's tiles (a uniform byte offset).
-template <int WAUX>
-__device__ __forceinline__ void s_load(SStage& S, const SOps& O, int st, uint32_t gofs = 0) {
+template <int WAUX, int NT>
+__device__ __forceinline__ void s_load(SStage<NT>& S, const SOps<NT>& O, int st, uint32_t gofs = 0) {
   const uint32_t wo = (uint32_t)st * 2048 + gofs, xo = (uint32_t)st * 256;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -124,17 +127,20 @@ __device__ __forceinline__ void s_load(SStage& S, const SOps& O, int st, uint32_
     S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wt[rt] + 1024, wo);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    S.b[i].h[0] = buf_load16(O.x, O.xlo + i * 128, xo);
-    S.b[i].h[1] = buf_load16(O.x, O.xhi + i * 128, xo);
-  }
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      S.b[n][i].h[0] = buf_load16(O.x, O.xlo[n] + i * 128, xo);
+      S.b[n][i].h[1] = buf_load16(O.x, O.xlo[n] + 64 + i * 128, xo);
+    }
 }
 
 struct SScales {
   int lo[4], hi[4];  // steps 4q, 4q+1 (lo) and 4q+2, 4q+3 (hi) of each tile
 };
 
-__device__ __forceinline__ void s_load_scales(SScales& C, const SOps& O, int q, uint32_t gofs = 0) {
+template <int NT>
+__device__ __forceinline__ void s_load_scales(SScales& C, const SOps<NT>& O, int q, uint32_t gofs = 0) {
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const v2i v = buf_load8(O.ws, O.wst[rt], (uint32_t)q * 512 + gofs);
@@ -144,22 +150,26 @@ __device__ __forceinline__ void s_load_scales(SScales& C, const SOps& O, int q, 
 }
 
 // Step with in-quad index J (0..3): A scale byte 2 * (J % 2) + i of the
-// (lo | hi) dword, B scale byte 2 * (J % 2) + i of the pair's dword `sb`.
-template <int J>
-__device__ __forceinline__ void s_mma(v4f (&acc)[4], const SStage& S, const SScales& C, int sb) {
+// (lo | hi) dword, B scale byte 2 * (J % 2) + i of token tile n's dword sb[n].
+template <int J, int NT>
+__device__ __forceinline__ void s_mma(v4f (&acc)[4][NT], const SStage<NT>& S, const SScales& C, const int (&sb)[NT]) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int sa = (J < 2) ? C.lo[rt] : C.hi[rt];
-    acc[rt] = mfma_ij<2 * (J % 2), 2 * (J % 2)>(S.a[rt][0], S.b[0].v, acc[rt], sa, sb);
-  }
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int sa = (J < 2) ? C.lo[rt] : C.hi[rt];
-    acc[rt] = mfma_ij<2 * (J % 2) + 1, 2 * (J % 2) + 1>(S.a[rt][1], S.b[1].v, acc[rt], sa, sb);
-  }
+    for (int rt = 0; rt < 4; ++rt) {
+      const int sa = (J < 2) ? C.lo[rt] : C.hi[rt];
+      acc[rt][n] = mfma_ij<2 * (J % 2), 2 * (J % 2)>(S.a[rt][0], S.b[n][0].v, acc[rt][n], sa, sb[n]);
+    }
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int sa = (J < 2) ? C.lo[rt] : C.hi[rt];
+      acc[rt][n] = mfma_ij<2 * (J % 2) + 1, 2 * (J % 2) + 1>(S.a[rt][1], S.b[n][1].v, acc[rt][n], sa, sb[n]);
+    }
 }
 
-// One token tile against G groups of four weight tiles each (group g at
+// NT token tiles against G groups of four weight tiles each (group g at
 // byte offsets g * gd in the data and g * sgd in the scales), streamed back
 // to back: all S4 (a multiple of 4) K steps of group 0, then of group 1, ...
 // Operand stages run two steps ahead and scale quads one quad ahead across
@@ -167,14 +177,14 @@ __device__ __forceinline__ void s_mma(v4f (&acc)[4], const SStage& S, const SSca
 // no branches (its last loads re-read the final steps and are never used).
 // After a group's last step epi(g, acc) consumes its results and acc restarts
 // at zero.  WAUX: cache policy of the weight loads.
-template <int WAUX, int G, typename Epi>
-__device__ __forceinline__ void stream_groups(v4f (&acc)[4], const SOps& O, int S4, uint32_t gd, uint32_t sgd,
+template <int WAUX, int G, int NT, typename Epi>
+__device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT>& O, int S4, uint32_t gd, uint32_t sgd,
                                               Epi&& epi) {
-  SStage s0, s1;
+  SStage<NT> s0, s1;
   SScales c0, c1;
   const int nq = S4 / 4, NQ = G * nq, V = G * S4;
   static_assert(G == 1 || G == 2, "one or two groups");
-  auto ld = [&](SStage& S, int v) {
+  auto ld = [&](SStage<NT>& S, int v) {
     const int g = (G > 1 && v >= S4) ? 1 : 0;
     s_load<WAUX>(S, O, v - g * S4, g ? gd : 0u);
   };
@@ -190,8 +200,12 @@ __device__ __forceinline__ void stream_groups(v4f (&acc)[4], const SOps& O, int 
   for (int g = 0; g < G; ++g) {
     for (int q = 0; q < nq; ++q) {
       const int st = 4 * q, v = g * S4 + st, vq = g * nq + q;
-      const int sb0 = *reinterpret_cast<const int*>(O.sxs + 2 * st);
-      const int sb1 = *reinterpret_cast<const int*>(O.sxs + 2 * st + 4);
+      int sb0[NT], sb1[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        sb0[n] = *reinterpret_cast<const int*>(O.sxs[n] + 2 * st);
+        sb1[n] = *reinterpret_cast<const int*>(O.sxs[n] + 2 * st + 4);
+      }
       s_mma<0>(acc, s0, c0, sb0);
       ld(s0, min(v + 2, V - 2));
       s_mma<1>(acc, s1, c0, sb0);
@@ -205,20 +219,26 @@ __device__ __forceinline__ void stream_groups(v4f (&acc)[4], const SOps& O, int 
     }
     epi(g, acc);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// One group: all S4 steps of one token tile, results left in acc.
-template <int WAUX>
-__device__ __forceinline__ void stream_tile(v4f (&acc)[4], const SOps& O, int S4) {
-  v4f res[4];
-  stream_groups<WAUX, 1>(acc, O, S4, 0u, 0u, [&](int, const v4f(&a)[4]) {
+// One group: all S4 steps of NT token tiles, results left in acc.
+template <int WAUX, int NT>
+__device__ __forceinline__ void stream_tile(v4f (&acc)[4][NT], const SOps<NT>& O, int S4) {
+  v4f res[4][NT];
+  stream_groups<WAUX, 1>(acc, O, S4, 0u, 0u, [&](int, const v4f(&a)[4][NT]) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) res[rt] = a[rt];
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) res[rt][n] = a[rt][n];
   });
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) acc[rt] = res[rt];
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[rt][n] = res[rt][n];
 }
 
 constexpr int kMaxSteps = 64;    // K <= 16384
@@ -288,13 +308,13 @@ __device__ int slot_pairs(const int32_t* __restrict__ phys, int np, int q, int* 
   return run;
 }
 
-// Stage a token tile's 128-column scales in LDS: 16 rows of 2 * S4 bytes,
-// zero beyond K/128 (padded steps) and beyond the tile's rows.
+// Stage the token tiles' 128-column scales in LDS: `rows` rows of 2 * S4
+// bytes, zero beyond K/128 (padded steps) and beyond the tiles' rows.
 template <typename Src>
 __device__ __forceinline__ void stage_token_scales(uint8_t* s_xs, const uint8_t* xs, int nrow, int nb, int S4,
-                                                   Src src) {
+                                                   int rows, Src src) {
   const int pitch = 2 * S4;
-  for (int i = threadIdx.x; i < 16 * pitch; i += blockDim.x) {
+  for (int i = threadIdx.x; i < rows * pitch; i += blockDim.x) {
     const int r = i / pitch, c = i - r * pitch;
     s_xs[i] = (r < nrow && c < nb) ? xs[(size_t)src(r) * nb + c] : (uint8_t)0;
   }
@@ -329,23 +349,21 @@ __device__ __forceinline__ SlotRows<PAIRS> slot_rows(const int32_t* offsets, con
   return R;
 }
 
-// The token operand of one 16-row tile: a buffer over the input rows and
-// this lane's byte offsets.  Lanes past the tile's rows read zeros (pair-
-// indexed: an offset past the buffer) or row 0 of the tile (bucketed); their
-// results are never stored.
-template <bool PAIRS>
-__device__ __forceinline__ void token_operand(SOps& O, const uint8_t* x, const SlotRows<PAIRS>& R, int tt0, int nrow,
-                                              int nsrc, int K, int l16, int g) {
-  const bool tv = l16 < nrow;
-  if (PAIRS) {
-    const uint32_t lim = (uint32_t)nsrc * (uint32_t)K;
-    O.x = make_rsrc(x, lim);
-    O.xlo = tv ? (uint32_t)R.src(tt0 + l16) * (uint32_t)K + (uint32_t)g * 16 : lim;
-  } else {
-    O.x = make_rsrc(x + (size_t)(R.row0 + tt0) * K, (uint32_t)nrow * K);
-    O.xlo = (tv ? (uint32_t)l16 : 0u) * (uint32_t)K + (uint32_t)g * 16;
+// The token operand of NT 16-row tiles (rows tt0 .. tt0 + nrow - 1 of the
+// slot): a buffer over the input rows and this lane's byte offsets.  Lanes
+// past the rows read zeros (an offset past the buffer); their results are
+// never stored.
+template <bool PAIRS, int NT>
+__device__ __forceinline__ void token_operand(SOps<NT>& O, const uint8_t* x, const SlotRows<PAIRS>& R, int tt0,
+                                              int nrow, int nsrc, int K, int l16, int g) {
+  const uint32_t lim = PAIRS ? (uint32_t)nsrc * (uint32_t)K : (uint32_t)nrow * (uint32_t)K;
+  O.x = PAIRS ? make_rsrc(x, lim) : make_rsrc(x + (size_t)(R.row0 + tt0) * K, lim);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int r = n * 16 + l16;
+    const uint32_t row = PAIRS ? (uint32_t)R.src(tt0 + (r < nrow ? r : 0)) : (uint32_t)r;
+    O.xlo[n] = r < nrow ? row * (uint32_t)K + (uint32_t)g * 16 : lim;
   }
-  O.xhi = O.xlo + 64;
 }
 
 // ---------------------------------------------------------------------------
@@ -357,17 +375,18 @@ __device__ __forceinline__ void token_operand(SOps& O, const uint8_t* x, const S
 //   pair-indexed (PAIRS true): xq/xs are per-token rows [nsrc = T], aq/as
 //   per-pair rows [T*k]; the slot's pairs come from phys[0, np).
 // ---------------------------------------------------------------------------
-template <bool PAIRS>
-__global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restrict__ xq,
-                                                         const uint8_t* __restrict__ xs,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ phys, int np, int k, int p0,
-                                                         int nsrc, const uint8_t* __restrict__ pw1,
-                                                         const uint8_t* __restrict__ pw1s, uint8_t* __restrict__ aq,
-                                                         uint8_t* __restrict__ as_, int32_t* __restrict__ counts,
-                                                         int H, int F) {
-  __shared__ float s_amax[4][16];
-  __shared__ __align__(16) uint8_t s_xs[16 * 2 * kMaxSteps];
+// NT 16-row token tiles share each pass over the block's weights (a slot
+// with more rows streams its weights once per 16 NT rows); NT = 2 needs more
+// registers and runs two blocks per CU instead of three.
+template <bool PAIRS, int NT>
+__global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm1_stream(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ phys, int np, int k, int p0, int nsrc, const uint8_t* __restrict__ pw1,
+    const uint8_t* __restrict__ pw1s, uint8_t* __restrict__ aq, uint8_t* __restrict__ as_,
+    int32_t* __restrict__ counts, int H, int F) {
+  constexpr int kRows = 16 * NT;  // token rows per pass
+  __shared__ float s_amax[4][kRows];
+  __shared__ __align__(16) uint8_t s_xs[kRows * 2 * kMaxSteps];
   __shared__ int s_list[PAIRS ? kPairRows : 1];
   __shared__ int s_cnt[2][4];
   const int nfb = F / kActBlock;
@@ -383,7 +402,7 @@ __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restri
   const int S4 = (int)G.steps;
   const int nb = H / kActBlock;
   const int f0 = fb * kActBlock + wave * 32;
-  SOps O;
+  SOps<NT> O;
   O.w = make_rsrc(pw1 + (size_t)s * G.data_slot, (uint32_t)G.data_slot);
   O.ws = make_rsrc(pw1s + (size_t)s * G.scale_slot, (uint32_t)G.scale_slot);
   const int tile[4] = {f0 / 16, f0 / 16 + 1, (F + f0) / 16, (F + f0) / 16 + 1};
@@ -392,43 +411,51 @@ __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restri
     O.wt[rt] = (uint32_t)tile[rt] * (uint32_t)G.data_tile + 16u * lane;
     O.wst[rt] = (uint32_t)tile[rt] * (uint32_t)G.scale_tile + 8u * lane;
   }
-  for (int tt0 = 0; tt0 < n; tt0 += 16) {
-    const int tok = tt0 + l16;
-    const bool tv = tok < n;
-    const int nrow = min(16, n - tt0);
-    __syncthreads();  // previous tile's readers of s_xs / s_amax are done
-    stage_token_scales(s_xs, xs, nrow, nb, S4, [&](int r) { return R.src(tt0 + r); });
+  for (int tt0 = 0; tt0 < n; tt0 += kRows) {
+    const int nrow = min(kRows, n - tt0);
+    __syncthreads();  // previous pass's readers of s_xs / s_amax are done
+    stage_token_scales(s_xs, xs, nrow, nb, S4, kRows, [&](int r) { return R.src(tt0 + r); });
     __syncthreads();
-    token_operand<PAIRS>(O, xq, R, tt0, nrow, nsrc, H, l16, g);
-    O.sxs = s_xs + (tv ? l16 : 0) * 2 * S4;
-    v4f acc[4];
+    token_operand<PAIRS, NT>(O, xq, R, tt0, nrow, nsrc, H, l16, g);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) O.sxs[t] = s_xs + (t * 16 + l16) * 2 * S4;
+    v4f acc[4][NT];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0.f, 0.f, 0.f, 0.f};
     stream_tile<MOE_G1_WAUX>(acc, O, S4);
     // SwiGLU: acc[0]/acc[2] are gate/up of columns f0 + 4g + r, acc[1]/acc[3] of f0 + 16 + 4g + r
-    float act[8];
+    float act[NT][8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      act[r] = silu(acc[0][r]) * acc[2][r];
-      act[4 + r] = silu(acc[1][r]) * acc[3][r];
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        act[t][r] = silu(acc[0][t][r]) * acc[2][t][r];
+        act[t][4 + r] = silu(acc[1][t][r]) * acc[3][t][r];
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(act[t][i]));
+      am = fmaxf(am, __shfl_xor(am, 16));
+      am = fmaxf(am, __shfl_xor(am, 32));
+      if (g == 0) s_amax[wave][t * 16 + l16] = am;
     }
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(act[i]));
-    am = fmaxf(am, __shfl_xor(am, 16));
-    am = fmaxf(am, __shfl_xor(am, 32));
-    if (g == 0) s_amax[wave][l16] = am;
     __syncthreads();
-    am = fmaxf(fmaxf(s_amax[0][l16], s_amax[1][l16]), fmaxf(s_amax[2][l16], s_amax[3][l16]));
-    const int e = scale_exp(am);
-    if (tv) {
-      const size_t d = (size_t)R.dst(tok);
-      uint8_t* ap = aq + d * F + f0 + 4 * g;
-      *reinterpret_cast<uint32_t*>(ap) =
-          pack4_fp8(ldexpf(act[0], -e), ldexpf(act[1], -e), ldexpf(act[2], -e), ldexpf(act[3], -e));
-      *reinterpret_cast<uint32_t*>(ap + 16) =
-          pack4_fp8(ldexpf(act[4], -e), ldexpf(act[5], -e), ldexpf(act[6], -e), ldexpf(act[7], -e));
-      if (wave == 0 && g == 0) as_[d * nfb + fb] = (uint8_t)(e + 127);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = t * 16 + l16;
+      const float am = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
+      const int e = scale_exp(am);
+      if (r < nrow) {
+        const size_t d = (size_t)R.dst(tt0 + r);
+        uint8_t* ap = aq + d * F + f0 + 4 * g;
+        *reinterpret_cast<uint32_t*>(ap) =
+            pack4_fp8(ldexpf(act[t][0], -e), ldexpf(act[t][1], -e), ldexpf(act[t][2], -e), ldexpf(act[t][3], -e));
+        *reinterpret_cast<uint32_t*>(ap + 16) =
+            pack4_fp8(ldexpf(act[t][4], -e), ldexpf(act[t][5], -e), ldexpf(act[t][6], -e), ldexpf(act[t][7], -e));
+        if (wave == 0 && g == 0) as_[d * nfb + fb] = (uint8_t)(e + 127);
+      }
     }
   }
 }
@@ -442,15 +469,13 @@ __global__ __launch_bounds__(256, 3) void k_gemm1_stream(const uint8_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int kG2Rows = 512;
 
-template <bool PAIRS>
-__global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restrict__ aq,
-                                                         const uint8_t* __restrict__ as_,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ phys, int np, int p0, int nsrc,
-                                                         const uint8_t* __restrict__ pw2,
-                                                         const uint8_t* __restrict__ pw2s, float* __restrict__ y,
-                                                         int H, int F) {
-  __shared__ __align__(16) uint8_t s_xs[16 * 2 * kMaxSteps];
+template <bool PAIRS, int NT>
+__global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
+    const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ phys, int np, int p0, int nsrc, const uint8_t* __restrict__ pw2,
+    const uint8_t* __restrict__ pw2s, float* __restrict__ y, int H, int F) {
+  constexpr int kRows = 16 * NT;  // token rows per pass
+  __shared__ __align__(16) uint8_t s_xs[kRows * 2 * kMaxSteps];
   __shared__ int s_list[PAIRS ? kPairRows : 1];
   __shared__ int s_cnt[2][4];
   const int nhb = (H + kG2Rows - 1) / kG2Rows;
@@ -466,7 +491,7 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
   const PackGeom G = pack_geom((uint32_t)H, (uint32_t)F);
   const int S4 = (int)G.steps;
   const int nb = F / kActBlock;
-  SOps O;
+  SOps<NT> O;
   O.w = make_rsrc(pw2 + (size_t)s * G.data_slot, (uint32_t)G.data_slot);
   O.ws = make_rsrc(pw2s + (size_t)s * G.scale_slot, (uint32_t)G.scale_slot);
 #pragma unroll
@@ -476,58 +501,80 @@ __global__ __launch_bounds__(256, 3) void k_gemm2_stream(const uint8_t* __restri
     O.wst[rt] = tile * (uint32_t)G.scale_tile + 8u * lane;
   }
   const uint32_t gd = 4u * (uint32_t)G.data_tile, sgd = 4u * (uint32_t)G.scale_tile;
-  for (int tt0 = 0; tt0 < n; tt0 += 16) {
-    const int tok = tt0 + l16;
-    const bool tv = tok < n;
-    const int nrow = min(16, n - tt0);
+  for (int tt0 = 0; tt0 < n; tt0 += kRows) {
+    const int nrow = min(kRows, n - tt0);
     __syncthreads();
-    stage_token_scales(s_xs, as_, nrow, nb, S4, [&](int r) { return R.src(tt0 + r); });
+    stage_token_scales(s_xs, as_, nrow, nb, S4, kRows, [&](int r) { return R.src(tt0 + r); });
     __syncthreads();
     if (!live) continue;
-    token_operand<PAIRS>(O, aq, R, tt0, nrow, nsrc, F, l16, g);
-    O.sxs = s_xs + (tv ? l16 : 0) * 2 * S4;
-    float* yr = tv ? y + (size_t)R.dst(tok) * H + h0 + 4 * g : nullptr;
-    v4f acc[4];
+    token_operand<PAIRS, NT>(O, aq, R, tt0, nrow, nsrc, F, l16, g);
+    float* yr[NT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_groups<MOE_G2_WAUX, 2>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4]) {
-      if (tv) {
+    for (int t = 0; t < NT; ++t) {
+      const int r = t * 16 + l16;
+      O.sxs[t] = s_xs + r * 2 * S4;
+      yr[t] = r < nrow ? y + (size_t)R.dst(tt0 + r) * H + h0 + 4 * g : nullptr;
+    }
+    v4f acc[4][NT];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    stream_groups<MOE_G2_WAUX, 2>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4][NT]) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (yr[t] == nullptr) continue;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-          *reinterpret_cast<float4*>(yr + 64 * grp + 16 * rt) = make_float4(a[rt][0], a[rt][1], a[rt][2], a[rt][3]);
+          *reinterpret_cast<float4*>(yr[t] + 64 * grp + 16 * rt) =
+              make_float4(a[rt][t][0], a[rt][t][1], a[rt][t][2], a[rt][t][3]);
       }
     });
   }
 }
 
 hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
-                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
+                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local, int nt,
                                hipStream_t st) {
-  k_gemm1_stream<false><<<P_local * (F / kActBlock), 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s,
-                                                                   aq, as, nullptr, H, F);
+  const unsigned grid = (unsigned)(P_local * (F / kActBlock));
+  if (nt >= 2)
+    k_gemm1_stream<false, 2><<<grid, 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s, aq, as, nullptr, H, F);
+  else
+    k_gemm1_stream<false, 1><<<grid, 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s, aq, as, nullptr, H, F);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                               const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
-  k_gemm2_stream<false><<<P_local * ((H + kG2Rows - 1) / kG2Rows), 256, 0, st>>>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y,
-                                                                     H, F);
+                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
+  const unsigned grid = (unsigned)(P_local * ((H + kG2Rows - 1) / kG2Rows));
+  if (nt >= 2)
+    k_gemm2_stream<false, 2><<<grid, 256, 0, st>>>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y, H, F);
+  else
+    k_gemm2_stream<false, 1><<<grid, 256, 0, st>>>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y, H, F);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int32_t* counts,
-                              int H, int F, int P_local, hipStream_t st) {
-  k_gemm1_stream<true><<<P_local * (F / kActBlock), 256, 0, st>>>(xq_tok, xs_tok, nullptr, phys, T * k, k, p0, T,
-                                                                  pw1, pw1s, aq, as, counts, H, F);
+                              int H, int F, int P_local, int nt, hipStream_t st) {
+  const unsigned grid = (unsigned)(P_local * (F / kActBlock));
+  if (nt >= 2)
+    k_gemm1_stream<true, 2><<<grid, 256, 0, st>>>(xq_tok, xs_tok, nullptr, phys, T * k, k, p0, T, pw1, pw1s, aq, as,
+                                                   counts, H, F);
+  else
+    k_gemm1_stream<true, 1><<<grid, 256, 0, st>>>(xq_tok, xs_tok, nullptr, phys, T * k, k, p0, T, pw1, pw1s, aq, as,
+                                                   counts, H, F);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
-                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local,
+                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt,
                               hipStream_t st) {
-  k_gemm2_stream<true><<<P_local * ((H + kG2Rows - 1) / kG2Rows), 256, 0, st>>>(aq, as, nullptr, phys, T * k, p0, T * k, pw2,
-                                                                    pw2s, y, H, F);
+  const unsigned grid = (unsigned)(P_local * ((H + kG2Rows - 1) / kG2Rows));
+  if (nt >= 2)
+    k_gemm2_stream<true, 2><<<grid, 256, 0, st>>>(aq, as, nullptr, phys, T * k, p0, T * k, pw2, pw2s, y, H, F);
+  else
+    k_gemm2_stream<true, 1><<<grid, 256, 0, st>>>(aq, as, nullptr, phys, T * k, p0, T * k, pw2, pw2s, y, H, F);
   return hipGetLastError();
 }
 

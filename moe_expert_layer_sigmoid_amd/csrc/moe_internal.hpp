@@ -49,11 +49,13 @@ hipError_t launch_combine_pairs(int T, int H, int k, const float* y, const int32
 // [P, R, K/2] + [P, R, K/32] into it.
 hipError_t launch_pack(const uint8_t* w, const uint8_t* ws, uint8_t* pw, uint8_t* ps, int P, int R, int K,
                        hipStream_t st);
+// Streaming GEMMs: `nt` (1 or 2) 16-row token tiles share each pass over a
+// block's weights.
 hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
-                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
+                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local, int nt,
                                hipStream_t st);
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                               const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
+                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st);
 // Pair-indexed GEMMs: each block lists its slot's pairs from phys [T*k].
 // GEMM1 reads per-token rows xq_tok/xs_tok and writes pair rows aq/as
 // [T*k, F]; GEMM2 reads those and writes pair rows y [T*k, H].  T <= 1024.
@@ -61,9 +63,9 @@ constexpr int kPairMaxT = 1024;
 // GEMM1 also writes each slot's pair count into counts [P_local].
 hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int32_t* counts,
-                              int H, int F, int P_local, hipStream_t st);
+                              int H, int F, int P_local, int nt, hipStream_t st);
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
-                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local,
+                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt,
                               hipStream_t st);
 // Large-M: persistent tiled kernels.  Their LDS (operand rings plus the
 // block's token scales) must fit a CU's 160 KB, which holds for

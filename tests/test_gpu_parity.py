@@ -50,17 +50,21 @@ def test_tiny_all_paths(path):
     assert res["chosen"] == ("small_m" if path == "auto" else path)
 
 
-def test_mid_remote_pairs_and_ragged_tiles():
+# With ~50 rows per slot, the large-input path runs its persistent tiled
+# GEMMs (partial token blocks, and with F = H = 384 partial weight blocks).
+@pytest.mark.parametrize("path", ["auto", "large_m"])
+def test_mid_remote_pairs_and_ragged_tiles(path):
     # 200 tokens (ragged against 64-token chunks and 16-token tiles), half the
     # slots remote, ~50 rows per slot (several token tiles)
-    _full_check(synth.make_custom(T=200, H=512, F=256, E=16, k=4, P_local=8, p0=4, seed=11))
+    _full_check(synth.make_custom(T=200, H=512, F=256, E=16, k=4, P_local=8, p0=4, seed=11), path)
 
 
-def test_odd_widths_and_eplb_replicas():
+@pytest.mark.parametrize("path", ["auto", "large_m"])
+def test_odd_widths_and_eplb_replicas(path):
     # H/128 = 3 and F/128 = 3 (one 32-block group per lane, partial 256-row block
     # of H), replicas over 2 ranks, a non-zero global token id base
     _full_check(synth.make_custom(T=300, H=384, F=384, E=12, k=3, P_local=8, p0=8, redundant=4, ranks=2,
-                                  seed=12, token_id_base=123456))
+                                  seed=12, token_id_base=123456), path)
 
 
 def test_wide_k_and_many_experts():
