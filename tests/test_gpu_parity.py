@@ -77,6 +77,12 @@ def test_single_token_and_capacity_bucket():
     _full_check(wl)
 
 
+@pytest.mark.parametrize("path", ["auto", "staged"])
+def test_few_touched_slots_narrow_gemms(path):
+    # fewer pairs than slots: GEMM2 runs 256-row blocks (H = 3072: 12 per slot)
+    _full_check(synth.make_custom(T=8, H=3072, F=512, E=64, k=6, P_local=16, p0=8, seed=21), path)
+
+
 def test_small_m_at_its_token_limit():
     # 1024 tokens each routed to all 16 experts: every slot lists 1024 pairs,
     # the small-input path's capacity
