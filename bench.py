@@ -300,9 +300,9 @@ def main():
                    "T": d.T, "H": d.H, "F": d.F, "E": d.E, "k": d.k, "P_local": d.P_local,
                    "path": r["chosen"], "touched_slots": r["touched"], "rows": r["rows"],
                    "weight_copies": args.copies},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm1_stream<true>", "achieved": round(g1_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_gemm1_stream<true, 1>", "achieved": round(g1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile("k_gemm1_stream<true>", args.workload),
+                     "traffic": traffic_from_profile("k_gemm1_stream<true, 1>", args.workload),
                      "bytes_per_launch": g1_bytes, "avg_launch_us": round(r["gemm1_us"], 2)},
         "layer_roofline": {"bound": "hbm", "achieved": round(lay_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(lay_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": lay_bytes,

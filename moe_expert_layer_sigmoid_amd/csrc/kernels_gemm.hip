@@ -246,12 +246,7 @@ constexpr int kMaxSteps = 64;    // K <= 16384
 // Cache policy of the streamed weight loads: non-temporal (each weight byte
 // is read once per call).  Measured on the decode share (512 tokens, 48
 // slots): GEMM1 5.4 -> 6.3 TB/s, GEMM2 (512-row blocks) 4.9 -> 5.2 TB/s.
-#ifndef MOE_G1_WAUX
-#define MOE_G1_WAUX 2
-#endif
-#ifndef MOE_G2_WAUX
-#define MOE_G2_WAUX 2
-#endif
+constexpr int kWeightAux = 2;
 constexpr int kPairRows = kPairMaxT;  // rows of one slot on the pair-indexed path
 
 // The pairs (t, j) whose physical slot is q, ascending, into list[0, cap);
@@ -424,7 +419,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm1_stream(
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_tile<MOE_G1_WAUX>(acc, O, S4);
+    stream_tile<kWeightAux>(acc, O, S4);
     // SwiGLU: acc[0]/acc[2] are gate/up of columns f0 + 4g + r, acc[1]/acc[3] of f0 + 16 + 4g + r
     float act[NT][8];
 #pragma unroll
@@ -522,7 +517,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_groups<MOE_G2_WAUX, NG>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4][NT]) {
+    stream_groups<kWeightAux, NG>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4][NT]) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (yr[t] == nullptr) continue;
