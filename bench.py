@@ -92,14 +92,32 @@ def run_gpu(workload: str, steps: int, warmup: int, copies: int):
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     tw0 = time.perf_counter()
     ev0.record(st)
     for i in range(steps):
+        marks[i].record(st)
         step(i)
+    marks[steps].record(st)
     ev1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - tw0
     gpu_ms = ev0.elapsed_time(ev1)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+
+    # achievable HBM rate: a plain 1 GiB device-to-device copy (read + write)
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(st)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(st)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
 
     # dominant kernel (GEMM1 of the small-input path: the same kernel the
     # forward launches) alone, on the stream it is launched on, with the
@@ -122,7 +140,7 @@ def run_gpu(workload: str, steps: int, warmup: int, copies: int):
     torch.cuda.synchronize()
     g1_us = g0.elapsed_time(g1) * 1000.0 / steps
     return dict(d=d, wl=wl, chosen=chosen, touched=touched, rows=rows, wall=wall, gpu_ms=gpu_ms,
-                gemm1_us=g1_us)
+                gemm1_us=g1_us, per_step=per_step, copy_gbs=copy_gbs)
 
 
 def _time(fn, steps: int, warmup: int, stream) -> float:
@@ -142,9 +160,10 @@ def _time(fn, steps: int, warmup: int, stream) -> float:
 
 
 def run_sweep(steps: int, warmup: int, copies: int, only=None):
-    """The token-count sweep (decode-share shapes, AUTO path at each T) and
-    the EP-shaped prefill share (8 ranks x 8192 tokens into this GPU's 48
-    experts, LARGE_M).  One JSON line per point on stdout."""
+    """The token-count sweep (decode-share shapes, AUTO path at each T), the
+    EP-shaped prefill share (8 ranks x 8192 tokens into this GPU's 48
+    experts, LARGE_M) and the skewed-routing EPLB share (8192 tokens, 448
+    physical slots, 56 local).  One JSON line per point on stdout."""
     import torch
     import moe_expert_layer_sigmoid_amd as mx
     import synth
@@ -159,7 +178,9 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
     for _ in range(copies - 1):
         w.append(tuple(t.clone() for t in w[0]))
 
-    def point(wl, name, path="auto"):
+    def point(wl, name, path="auto", wts=None, extra=None):
+        wts = w if wts is None else wts
+        nw = len(wts)
         d = mx.Dims.of(wl.dims)
         x = torch.from_numpy(wl.x.view("int16")).to(dev)
         logits = torch.from_numpy(wl.logits).to(dev)
@@ -168,11 +189,11 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
         out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
         ws = mx.workspace(d)
         taps = mx.make_taps(d)
-        chosen = mx.moe_forward(d, x, logits, *w[0], rc, rs, out, ws, taps=taps, path=path)
+        chosen = mx.moe_forward(d, x, logits, *wts[0], rc, rs, out, ws, taps=taps, path=path)
         torch.cuda.synchronize()
         counts = taps["counts"].cpu().numpy()
         touched, rows = int((counts > 0).sum()), int(counts.sum())
-        ms = _time(lambda i: mx.moe_forward(d, x, logits, *w[i % copies], rc, rs, out, ws, path=path),
+        ms = _time(lambda i: mx.moe_forward(d, x, logits, *wts[i % nw], rc, rs, out, ws, path=path),
                    steps, warmup, st)
         lay = layer_bytes(d, touched)
         flops = 2 * rows * (2 * d.F * d.H + d.H * d.F)
@@ -183,15 +204,17 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
         if chosen == "large_m":
             # the two grouped GEMMs alone, through the component calls (bucketed rows)
             g1 = _time(lambda i: mx.moe_grouped_gemm1_swiglu(d, taps["xq"], taps["xs"], taps["offsets"],
-                                                             w[i % copies][0], w[i % copies][1], taps["aq"],
+                                                             wts[i % nw][0], wts[i % nw][1], taps["aq"],
                                                              taps["as_"], ws, stream=st), steps, warmup, st)
             g2c = _time(lambda i: mx.moe_grouped_gemm2_combine(d, taps["aq"], taps["as_"], taps["offsets"],
-                                                               w[i % copies][2], w[i % copies][3],
+                                                               wts[i % nw][2], wts[i % nw][3],
                                                                taps["row_of_pair"], taps["topk_w"], out, ws,
                                                                stream=st), steps, warmup, st)
             f1 = 2 * rows * 2 * d.F * d.H
             rec.update(gemm1_ms=round(g1, 4), gemm1_mfma_frac=round(f1 / (g1 * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                        gemm2_combine_ms=round(g2c, 4))
+        if extra:
+            rec.update(extra(d, ms))
         print(json.dumps(rec), flush=True)
         del ws, taps, out
 
@@ -199,28 +222,59 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
         if only is None or f"sweep_T{T}" in only:
             point(synth.make_sweep(T, with_weights=False), f"sweep_T{T}")
     if only is None or "prefill_ep8_rank_share" in only:
-        point(synth.make_ep_shaped(8, with_weights=False), "prefill_ep8_rank_share", path="large_m")
+        # tokens/s of one rank's share: its 8192 tokens per whole call
+        point(synth.make_ep_shaped(8, with_weights=False), "prefill_ep8_rank_share", path="large_m",
+              extra=lambda d, ms: {"rank_share_tokens_per_s": round(8192 / (ms * 1e-3), 1)})
+    if only is None or "eplb8192" in only:
+        del w[1:]
+        torch.cuda.empty_cache()
+        wl = synth.make("eplb8192")
+        de = mx.Dims.of(wl.dims)
+        nat = [torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
+        we = [mx.pack_weights(de, *nat)]
+        del nat
+        for _ in range(copies - 1):
+            we.append(tuple(t.clone() for t in we[0]))
+        point(wl, "eplb8192", wts=we, extra=lambda d, ms: {"P_total": d.P_total, "P_local": d.P_local})
+
+
+def _pct(sorted_vals, p: float) -> float:
+    """Percentile of an ascending list (nearest rank)."""
+    if not sorted_vals:
+        return float("nan")
+    i = min(len(sorted_vals) - 1, max(0, int(round(p / 100.0 * (len(sorted_vals) - 1)))))
+    return sorted_vals[i]
 
 
 def cpu_baseline(wl, n_slots: int):
     """The oracle (float64 NumPy) on a bounded sample: the whole front end for
     all tokens plus the expert work of the first ``n_slots`` local slots,
-    scaled to the full layer by P_local / n_slots."""
+    scaled to the full layer by P_local / n_slots; then the same with BLAS on
+    one thread over one slot."""
     from oracle import moe as om
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas = 1
+        blas, threadpool_limits = 1, None
+    d = wl.dims
     t0 = time.perf_counter()
     om.forward(wl, slots=range(n_slots))
     dt = time.perf_counter() - t0
-    d = wl.dims
     est = dt * d.P_local / n_slots
-    return {"value": round(d.T / est, 3), "unit": "tokens/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"oracle forward of {d.T} tokens with expert work on {n_slots} of {d.P_local} "
-                      f"local slots ({dt:.1f}s), scaled x{d.P_local / n_slots:g}"}
+    res = {"value": round(d.T / est, 3), "unit": "tokens/s", "cores": int(blas),
+           "kind": "oracle",
+           "sample": f"oracle forward of {d.T} tokens with expert work on {n_slots} of {d.P_local} "
+                     f"local slots ({dt:.1f}s), scaled x{d.P_local / n_slots:g}"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            om.forward(wl, slots=range(1))
+            dt1 = time.perf_counter() - t0
+        res["single_thread"] = {"value": round(d.T / (dt1 * d.P_local), 3), "unit": "tokens/s",
+                                "sample": f"the same with BLAS on one thread and expert work on 1 slot "
+                                          f"({dt1:.1f}s), scaled x{d.P_local}"}
+    return res
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -240,8 +294,8 @@ def traffic_from_profile(kernel: str, workload: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated over steps")
     ap.add_argument("--workload", default="decode512", help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -250,7 +304,7 @@ def main():
                     help="instead of the headline line: the token-count sweep and the EP-shaped prefill share, "
                          "one JSON line per point")
     ap.add_argument("--points", default=None,
-                    help="with --sweep: comma-separated point names (sweep_T<T>, prefill_ep8_rank_share)")
+                    help="with --sweep: comma-separated point names (sweep_T<T>, prefill_ep8_rank_share, eplb8192)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB with torch (a plain copy kernel of "
                          "known size, for scaling HBM byte counters under rocprofv3 --pmc)")
@@ -307,7 +361,10 @@ def main():
         "layer_roofline": {"bound": "hbm", "achieved": round(lay_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(lay_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": lay_bytes,
                            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 5),
-                           "gpu_event_ms_per_step": round(r["gpu_ms"] / args.steps, 4)},
+                           "gpu_event_ms_per_step": round(r["gpu_ms"] / args.steps, 4),
+                           "measured_copy_gbs": round(r["copy_gbs"], 1)},
+        "step_ms": {"median": round(_pct(r["per_step"], 50), 4), "p10": round(_pct(r["per_step"], 10), 4),
+                    "p90": round(_pct(r["per_step"], 90), 4)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(r["wl"], args.cpu_slots)
