@@ -245,7 +245,7 @@ constexpr int kMaxSteps = 64;    // K <= 16384
 
 // Cache policy of the streamed weight loads: non-temporal (each weight byte
 // is read once per call).  Measured on the decode share (512 tokens, 48
-// slots): GEMM1 5.4 -> 6.3 TB/s, GEMM2 (512-row blocks) 4.9 -> 5.2 TB/s.
+// slots): GEMM1 5.4 -> 6.3 TB/s, GEMM2 (then in 512-row blocks) 4.9 -> 5.2 TB/s.
 constexpr int kWeightAux = 2;
 constexpr int kPairRows = kPairMaxT;  // rows of one slot on the pair-indexed path
 
@@ -456,16 +456,16 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm1_stream(
 }
 
 // ---------------------------------------------------------------------------
-// a6: one block per (local slot s, block of 256 NG rows of H).  Wave w owns
-// rows hb*256NG + 64NG w + [0, 64NG) as NG groups of four 16-row tiles,
-// streamed back to back (512-row blocks, NG = 2, fill the chip in one round at
-// three blocks per CU: 7168 / 512 * 48 slots = 672 blocks; NG = 1 doubles the
-// blocks of each slot when few slots are touched).  y rows are f32 [rows, H]
-// (bucketed rows, or pair rows with the act rows pair-indexed too).
+// a6: one block per (local slot s, block of 256 rows of H).  Wave w owns rows
+// hb*256 + 64w + [0, 64) as one group of four 16-row tiles.  7168 / 256 * 48
+// slots = 1344 blocks at three per CU: blocks of 512 rows (two groups per wave,
+// one round over the chip) measured 5-8% slower at 512-1536 tokens.  y rows
+// are f32 [rows, H] (bucketed rows, or pair rows with the act rows
+// pair-indexed too).
 // ---------------------------------------------------------------------------
-constexpr int kG2Rows = 512;  // rows of H per block with two groups per wave (NG = 2)
+constexpr int kG2Rows = 256;  // rows of H per block
 
-template <bool PAIRS, int NT, int NG>
+template <bool PAIRS, int NT>
 __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ phys, int np, int p0, int nsrc, const uint8_t* __restrict__ pw2,
@@ -474,8 +474,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
   __shared__ __align__(16) uint8_t s_xs[kRows * 2 * kMaxSteps];
   __shared__ int s_list[PAIRS ? kPairRows : 1];
   __shared__ int s_cnt[2][4];
-  constexpr int kRowsB = kG2Rows / 2 * NG;  // rows of H per block
-  const int nhb = (H + kRowsB - 1) / kRowsB;
+  const int nhb = (H + kG2Rows - 1) / kG2Rows;
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nhb, hb = item - s * nhb;
   const SlotRows<PAIRS> R = slot_rows<PAIRS>(offsets, phys, np, p0 + s, s, 1, s_list, s_cnt);
@@ -483,8 +482,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
   if (n <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int h0 = hb * kRowsB + wave * 64 * NG;
-  const bool live = h0 < H;  // wave-uniform; H is a multiple of 128 (NG = 2: a live wave has 8 full tiles)
+  const int h0 = hb * kG2Rows + wave * 64;
+  const bool live = h0 < H;  // wave-uniform; H is a multiple of 128, so a live wave has 4 full tiles
   const PackGeom G = pack_geom((uint32_t)H, (uint32_t)F);
   const int S4 = (int)G.steps;
   const int nb = F / kActBlock;
@@ -517,7 +516,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_groups<kWeightAux, NG>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4][NT]) {
+    stream_groups<kWeightAux, 1>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4][NT]) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (yr[t] == nullptr) continue;
@@ -541,26 +540,20 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
   return hipGetLastError();
 }
 
-// GEMM2 blocks of 256 rows (one group of four tiles per wave, twice the
-// blocks per slot) when few slots are touched, 512 rows otherwise.
 template <bool PAIRS>
 static void gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const int32_t* phys, int np,
                          int p0, int nsrc, const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F,
-                         int P_local, int nt, bool narrow, hipStream_t st) {
-  const unsigned g2 = (unsigned)(P_local * ((H + kG2Rows - 1) / kG2Rows));
-  const unsigned g1 = (unsigned)(P_local * ((H + kG2Rows / 2 - 1) / (kG2Rows / 2)));
+                         int P_local, int nt, hipStream_t st) {
+  const unsigned grid = (unsigned)(P_local * ((H + kG2Rows - 1) / kG2Rows));
   if (nt >= 2)
-    k_gemm2_stream<PAIRS, 2, 2><<<g2, 256, 0, st>>>(aq, as, offsets, phys, np, p0, nsrc, pw2, pw2s, y, H, F);
-  else if (narrow)
-    k_gemm2_stream<PAIRS, 1, 1><<<g1, 256, 0, st>>>(aq, as, offsets, phys, np, p0, nsrc, pw2, pw2s, y, H, F);
+    k_gemm2_stream<PAIRS, 2><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, nsrc, pw2, pw2s, y, H, F);
   else
-    k_gemm2_stream<PAIRS, 1, 2><<<g2, 256, 0, st>>>(aq, as, offsets, phys, np, p0, nsrc, pw2, pw2s, y, H, F);
+    k_gemm2_stream<PAIRS, 1><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, nsrc, pw2, pw2s, y, H, F);
 }
 
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, bool narrow,
-                               hipStream_t st) {
-  gemm2_stream<false>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y, H, F, P_local, nt, narrow, st);
+                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
+  gemm2_stream<false>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y, H, F, P_local, nt, st);
   return hipGetLastError();
 }
 
@@ -579,8 +572,8 @@ hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, cons
 
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt,
-                              bool narrow, hipStream_t st) {
-  gemm2_stream<true>(aq, as, nullptr, phys, T * k, p0, T * k, pw2, pw2s, y, H, F, P_local, nt, narrow, st);
+                              hipStream_t st) {
+  gemm2_stream<true>(aq, as, nullptr, phys, T * k, p0, T * k, pw2, pw2s, y, H, F, P_local, nt, st);
   return hipGetLastError();
 }
 

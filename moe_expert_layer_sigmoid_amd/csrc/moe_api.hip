@@ -101,9 +101,6 @@ double mean_rows(const moe_dims_t* d) { return (double)d->T * d->k / d->P_total;
 // Token tiles per weight pass of the streaming GEMMs: two once a slot's rows
 // commonly exceed one 16-row tile.
 int stream_tiles(const moe_dims_t* d) { return mean_rows(d) > 10.0 ? 2 : 1; }
-// GEMM2 in 256-row blocks while fewer pairs than slots (most slots idle, few
-// blocks busy; measured 14.5 -> 10.2 us at 1 token).
-bool narrow_gemm2(const moe_dims_t* d) { return mean_rows(d) < 1.0; }
 // The large-input path streams weights while the slots' rows fit about one
 // two-tile pass (the 128-token tiles of the persistent kernels would be mostly
 // empty and their weight stream latency-bound), and runs the tiled kernels
@@ -124,8 +121,7 @@ hipError_t gemm1(moe_path_t p, const uint8_t* xq, const uint8_t* xs, const int32
 hipError_t gemm2(moe_path_t p, const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                  const uint8_t* pw2s, float* y, const moe_dims_t* d, hipStream_t st) {
   if (tiled_gemms(p, d)) return launch_gemm2_tiled(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st);
-  return launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, stream_tiles(d), narrow_gemm2(d),
-                             st);
+  return launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, stream_tiles(d), st);
 }
 // The component GEMM calls pick by token count like MOE_PATH_AUTO.
 moe_path_t gemm_path(const moe_dims_t* d) {
@@ -296,7 +292,7 @@ int moe_grouped_gemm2_combine_pairs(const moe_dims_t* d, const uint8_t* aq_pair,
   hipStream_t st = (hipStream_t)stream;
   float* y = at<float>(ws, layout_of(d).y);
   MOE_TRY(launch_gemm2_pairs(aq_pair, as_pair, phys_ids, d->T, d->k, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local,
-                             stream_tiles(d), narrow_gemm2(d), st));
+                             stream_tiles(d), st));
   MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys_ids, d->p0, d->P_local, topk_w, out, nullptr, 0,
                                d->P_total, nullptr, counts, offsets, st));
   return MOE_OK;
@@ -360,8 +356,7 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
     const int nt = stream_tiles(d);
     MOE_TRY(launch_gemm1_pairs(xq_tok, xs_tok, phys, d->T, d->k, d->p0, pw1, pw1s, aq_p, as_p, counts, d->H, d->F,
                                d->P_local, nt, st));
-    MOE_TRY(launch_gemm2_pairs(aq_p, as_p, phys, d->T, d->k, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local, nt,
-                               narrow_gemm2(d), st));
+    MOE_TRY(launch_gemm2_pairs(aq_p, as_p, phys, d->T, d->k, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local, nt, st));
     MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys, d->p0, d->P_local, w, out, partial,
                                  (d->T + kFrontTokens - 1) / kFrontTokens, d->P_total, load_hist, counts, offsets,
                                  st));

@@ -54,11 +54,8 @@ hipError_t launch_pack(const uint8_t* w, const uint8_t* ws, uint8_t* pw, uint8_t
 hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
                                const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local, int nt,
                                hipStream_t st);
-// `narrow` (few touched slots): GEMM2 blocks of 256 rows instead of 512,
-// twice the blocks per slot.
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, bool narrow,
-                               hipStream_t st);
+                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st);
 // Pair-indexed GEMMs: each block lists its slot's pairs from phys [T*k].
 // GEMM1 reads per-token rows xq_tok/xs_tok and writes pair rows aq/as
 // [T*k, F]; GEMM2 reads those and writes pair rows y [T*k, H].  T <= 1024.
@@ -69,7 +66,7 @@ hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, cons
                               int H, int F, int P_local, int nt, hipStream_t st);
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt,
-                              bool narrow, hipStream_t st);
+                              hipStream_t st);
 // Large-M: persistent tiled kernels.  Their LDS (operand rings plus the
 // block's token scales) must fit a CU's 160 KB, which holds for
 // H, F <= 8192: tiled_fits(H, F, P_local).

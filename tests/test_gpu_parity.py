@@ -78,8 +78,9 @@ def test_single_token_and_capacity_bucket():
 
 
 @pytest.mark.parametrize("path", ["auto", "staged"])
-def test_few_touched_slots_narrow_gemms(path):
-    # fewer pairs than slots: GEMM2 runs 256-row blocks (H = 3072: 12 per slot)
+def test_few_touched_slots(path):
+    # fewer pairs than slots: most GEMM blocks find their slot empty and
+    # return at once (H = 3072: 12 GEMM2 blocks of 256 rows per slot)
     _full_check(synth.make_custom(T=8, H=3072, F=512, E=64, k=6, P_local=16, p0=8, seed=21), path)
 
 
