@@ -67,6 +67,21 @@ def test_odd_widths_and_eplb_replicas(path):
                                   seed=12, token_id_base=123456), path)
 
 
+def test_tiled_several_token_blocks_per_slot():
+    # ~250 rows per slot: two or three 128-token blocks per slot, the last
+    # one ragged
+    res = _full_check(synth.make_custom(T=1000, H=512, F=1024, E=16, k=4, P_local=8, p0=4, seed=22), "large_m")
+    assert res["chosen"] == "large_m"
+
+
+def test_tiled_skewed_slots():
+    # Zipf popularity: the popular slots span up to five token blocks, the
+    # rest one partial block
+    wl = synth.make_custom(T=600, H=1024, F=512, E=16, k=4, P_local=8, p0=0, seed=23, zipf_s=1.2)
+    res = _full_check(wl, "large_m")
+    assert res["counts"].max() > 512 and res["chosen"] == "large_m"
+
+
 def test_wide_k_and_many_experts():
     # k = 16 of 1024 experts (16 logits per lane), skewed popularity
     _full_check(synth.make_custom(T=96, H=256, F=128, E=1024, k=16, P_local=64, p0=0, seed=13, zipf_s=1.2))
@@ -248,6 +263,12 @@ def test_decode_share_512_tokens(path):
 
 def test_prefill_share_8192_tokens():
     res = _big_check(synth.make("prefill8192"))
+    assert res["chosen"] == "large_m"
+
+
+def test_sweep_16384_tokens():
+    # 256 mean rows per slot: two or three token blocks per slot at full width
+    res = _big_check(synth.make_sweep(16384), n_slots=2, n_tokens=8)
     assert res["chosen"] == "large_m"
 
 
