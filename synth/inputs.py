@@ -172,22 +172,23 @@ def _encode_mxfp4(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 # Expert weights (cached per process: the 7168/2048 family is shared by every full-size workload)
 # ----------------------------------------------------------------------------
 
-_W_CACHE: Dict[Tuple[int, int, int, int], Tuple[np.ndarray, ...]] = {}
+_W_CACHE: Dict[tuple, Tuple[np.ndarray, ...]] = {}
 _W_LOCK = threading.Lock()
 
 
-def _expert_weights(weights_key: int, H: int, F: int, e: int) -> Tuple[np.ndarray, ...]:
-    ck = (weights_key, H, F, e)
+def _expert_weights(weights_key: int, H: int, F: int, e: int,
+                    std: Tuple[float, float] = (W_STD, W_STD)) -> Tuple[np.ndarray, ...]:
+    ck = (weights_key, H, F, e, std)
     with _W_LOCK:
         hit = _W_CACHE.get(ck)
     if hit is not None:
         return hit
     g1 = _rng(weights_key, STREAM_W, e, 1)
-    w1f = (g1.standard_normal((2 * F, H), dtype=np.float32) * np.float32(W_STD))
+    w1f = (g1.standard_normal((2 * F, H), dtype=np.float32) * np.float32(std[0]))
     w1, w1s = _encode_mxfp4(w1f)
     del w1f
     g2 = _rng(weights_key, STREAM_W, e, 2)
-    w2f = (g2.standard_normal((H, F), dtype=np.float32) * np.float32(W_STD))
+    w2f = (g2.standard_normal((H, F), dtype=np.float32) * np.float32(std[1]))
     w2, w2s = _encode_mxfp4(w2f)
     del w2f
     out = (w1, w1s, w2, w2s)
@@ -201,7 +202,8 @@ def clear_cache() -> None:
         _W_CACHE.clear()
 
 
-def _slot_weights(weights_key: int, H: int, F: int, slot_expert: np.ndarray):
+def _slot_weights(weights_key: int, H: int, F: int, slot_expert: np.ndarray,
+                  std: Tuple[float, float] = (W_STD, W_STD)):
     P = len(slot_expert)
     w1 = np.empty((P, 2 * F, H // 2), np.uint8)
     w1s = np.empty((P, 2 * F, H // 32), np.uint8)
@@ -209,7 +211,7 @@ def _slot_weights(weights_key: int, H: int, F: int, slot_expert: np.ndarray):
     w2s = np.empty((P, H, F // 32), np.uint8)
     uniq = sorted(set(int(e) for e in slot_expert))
     with _cf.ThreadPoolExecutor(_workers()) as ex:
-        got = dict(zip(uniq, ex.map(lambda e: _expert_weights(weights_key, H, F, e), uniq)))
+        got = dict(zip(uniq, ex.map(lambda e: _expert_weights(weights_key, H, F, e, std), uniq)))
     for s, e in enumerate(slot_expert):
         a, b, c, d = got[int(e)]
         w1[s], w1s[s], w2[s], w2s[s] = a, b, c, d
@@ -408,11 +410,13 @@ def make_ep_shaped(ranks: int = 8, T_rank: int = 8192, with_weights: bool = True
 
 def make_custom(T: int, H: int, F: int, E: int, k: int, P_local: int, p0: int = 0,
                 redundant: int = 0, ranks: int = 1, seed: int = 100, token_id_base: int = 0,
-                T_max: Optional[int] = None, zipf_s: Optional[float] = None) -> Workload:
+                T_max: Optional[int] = None, zipf_s: Optional[float] = None,
+                w_std: Tuple[float, float] = (W_STD, W_STD)) -> Workload:
     """A workload of arbitrary shape (parity cases that span several tiles and
     ragged tails).  ``redundant`` > 0 adds replicas by the greedy map over a
     uniform (or Zipf, if ``zipf_s``) popularity; physical slots are spread over
-    ``ranks`` ranks and this GPU holds [p0, p0 + P_local)."""
+    ``ranks`` ranks and this GPU holds [p0, p0 + P_local).  ``w_std``: the
+    standard deviations of W1 and W2 (both 0.02 by default)."""
     pop = None
     bias = None
     if zipf_s is not None:
@@ -431,7 +435,7 @@ def make_custom(T: int, H: int, F: int, E: int, k: int, P_local: int, p0: int = 
         raise ValueError("local slot window out of range")
     slot_expert = all_slot_expert[p0:p0 + P_local].copy()
     logits, x = _tokens(seed, 0, T, H, E, bias)
-    w1, w1s, w2, w2s = _slot_weights(1000 + seed, H, F, slot_expert)
+    w1, w1s, w2, w2s = _slot_weights(1000 + seed, H, F, slot_expert, tuple(w_std))
     return Workload(name=f"custom_T{T}_H{H}_F{F}_E{E}_k{k}", dims=d, logits=logits, x=x,
                     rep_count=rep_count, rep_slots=rep_slots, slot_expert=slot_expert,
                     w1=w1, w1s=w1s, w2=w2, w2s=w2s, popularity=pop)

@@ -104,6 +104,13 @@ def test_host_validation_before_launch():
     # the small-input path beyond 1024 tokens is refused, not rerouted
     big = _dims(T=1025, T_max=1025)
     assert _forward_raw(big, GOOD, 0x100000, mx.moe_workspace_bytes(big), path=1)[0] == -2
+    # widths beyond 16384 are refused; the large-input path's tiled GEMMs stop
+    # at 8192 (their LDS), and AUTO then takes the staged path
+    assert _forward_raw(_dims(H=16512), GOOD, 0x100000, need)[0] == -2
+    wide = _dims(T=2048, T_max=2048, H=16384)
+    wneed = mx.moe_workspace_bytes(wide)
+    assert _forward_raw(wide, GOOD, 0x100000, wneed, path=3)[0] == -2
+    assert mx.moe_select_path(wide) == "staged"
 
 
 def test_zero_tokens_is_a_no_op():
