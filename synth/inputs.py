@@ -320,6 +320,29 @@ def greedy_replica_map(p: np.ndarray, redundant: int, ranks: int):
     return c.astype(np.int32), rep_slots, slot_expert
 
 
+def naive_replica_map(E: int, P_total: int):
+    """Naive placement (no load information): slot s holds logical expert
+    s mod E, so the P_total - E redundant slots copy experts 0, 1, ... in
+    order.  Returns (rep_count [E], rep_slots [E, R_max] (-1 pad),
+    slot_expert [P_total]); each expert's slots in ascending order."""
+    slot_expert = (np.arange(P_total) % E).astype(np.int32)
+    rep_count = np.bincount(slot_expert, minlength=E).astype(np.int32)
+    R_max = int(rep_count.max())
+    rep_slots = -np.ones((E, R_max), np.int32)
+    fill = np.zeros(E, np.int64)
+    for s, e in enumerate(slot_expert.tolist()):
+        rep_slots[e, fill[e]] = s
+        fill[e] += 1
+    return rep_count, rep_slots, slot_expert
+
+
+def skewed_logits(key: int, sub: int, T: int, E: int, k: int, s: float = 1.2) -> np.ndarray:
+    """Router logits whose expert popularity follows Zipf(s) (capped at 1/k):
+    N(0, 1) plus the per-expert bias of ``zipf_bias``."""
+    pop = zipf_popularity(E, k, s, _rng(key, STREAM_EPLB, 0))
+    return _tokens(key, sub, T, 128, E, zipf_bias(pop, k))[0]
+
+
 # ----------------------------------------------------------------------------
 # Public constructors
 # ----------------------------------------------------------------------------
