@@ -236,6 +236,61 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
         for _ in range(copies - 1):
             we.append(tuple(t.clone() for t in we[0]))
         point(wl, "eplb8192", wts=we, extra=lambda d, ms: {"P_total": d.P_total, "P_local": d.P_local})
+        del we
+        torch.cuda.empty_cache()
+    if only is None or "eplb_migrate448" in only:
+        eplb_migrate_point(steps, warmup)
+
+
+def eplb_migrate_point(steps: int, warmup: int):
+    """EPLB rebalance + weight migration on the skewed share's shape: record
+    the loads of 8192 Zipf-routed tokens on the naive 448-slot table with the
+    fused forward, rebalance (library host call, timed on the host), and time
+    the migration kernel that copies the new experts of rank 0's 56 slots
+    from a pool of all 384 packed experts (copy time does not depend on the
+    bytes, so the pool is zero-filled)."""
+    import numpy as np
+    import torch
+    import moe_expert_layer_sigmoid_amd as mx
+    import synth
+
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    c = synth.WORKLOADS["eplb8192"]
+    wl = synth.make("eplb8192", with_weights=False)
+    E, Pt, ranks = wl.dims.E, wl.dims.P_total, c["ranks"]
+    rc0, rs0, se0 = synth.naive_replica_map(E, Pt)
+    d = mx.Dims.of(wl.dims, R_max=rs0.shape[1])
+    per = [mx.moe_packed_bytes(d, i) // d.P_local for i in range(4)]
+    slots = [torch.zeros(per[i] * d.P_local, dtype=torch.uint8, device=dev) for i in range(4)]
+    hist = torch.zeros(Pt, dtype=torch.int32, device=dev)
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
+    mx.moe_forward(d, torch.from_numpy(wl.x.view("int16")).to(dev), torch.from_numpy(wl.logits).to(dev),
+                   *slots, torch.from_numpy(rc0).to(dev), torch.from_numpy(rs0).to(dev), out, mx.workspace(d),
+                   load_hist=hist)
+    h = hist.cpu().numpy()
+    t0 = time.perf_counter()
+    rc1, rs1, se1 = mx.moe_eplb_rebalance(E, Pt, ranks, 64, h, se0)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    loc = slice(d.p0, d.p0 + d.P_local)
+    src_np = np.where(se0[loc] == se1[loc], -1, se1[loc]).astype(np.int32)
+    moved = int((src_np >= 0).sum())
+    src = torch.from_numpy(src_np).to(dev)
+    pool = [torch.zeros(per[i] * E, dtype=torch.uint8, device=dev) for i in range(4)]
+    ms = _time(lambda i: mx.moe_eplb_migrate(d, src, E, pool, slots, stream=st), steps, warmup, st)
+    nbytes = 2 * moved * sum(per)
+    # the recorded batch's largest slot load before and after (same tokens)
+    after = torch.zeros(Pt, dtype=torch.int32, device=dev)
+    mx.moe_forward(mx.Dims.of(d, R_max=rs1.shape[1]), torch.from_numpy(wl.x.view("int16")).to(dev),
+                   torch.from_numpy(wl.logits).to(dev), *slots, torch.from_numpy(rc1).to(dev),
+                   torch.from_numpy(rs1).to(dev), out, mx.workspace(d), load_hist=after)
+    rec = {"point": "eplb_migrate448", "T": d.T, "P_total": Pt, "P_local": d.P_local, "moved_slots": moved,
+           "rebalance_host_ms": round(host_ms, 3), "migrate_ms": round(ms, 4),
+           "migrate_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "max_slot_load_before": int(h.max()), "max_slot_load_after": int(after.max().item()),
+           "mean_slot_load": round(float(h.mean()), 1)}
+    print(json.dumps(rec), flush=True)
 
 
 def _pct(sorted_vals, p: float) -> float:

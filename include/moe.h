@@ -237,6 +237,51 @@ int moe_forward(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, cons
                 uint16_t* out, const moe_taps_t* taps, moe_path_t* chosen,
                 void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* EPLB rebalance: a new replica table from the loads recorded by a2 (host
+ * call; every pointer is a HOST pointer; no stream, no device memory).
+ * The pages run EPLB with redundant physical experts and rebalance every few
+ * hundred steps from the recorded per-expert loads [sglang PR 35619,
+ * Summary and reviewer reproduction; FlyDSL issue 978, Benchmark plan and
+ * Data-quality gates]; they give no placement algorithm.  This one:
+ *  1. L_e = sum of load_hist[s] over the slots s with slot_expert_old[s] == e
+ *     (slots holding -1 are ignored);
+ *  2. every expert gets one replica; P_total - E times, the expert with the
+ *     largest L_e / c_e (exact comparison) among those with c_e < R_max gets
+ *     one more, equal shares to the lower e;
+ *  3. replicas in descending L_e / c_e (then e, then replica index) go one by
+ *     one to the rank (slots [r P_total/n_ranks, (r+1) P_total/n_ranks)) with
+ *     a free slot that does not hold e yet, else any rank with a free slot,
+ *     the one with the smallest load (f64 sum of the shares placed on it,
+ *     in placement order), then the lower rank;
+ *  4. inside a rank a replica keeps a slot that held e in the old map (the
+ *     lowest first), so that it needs no migration; the others fill the
+ *     rank's remaining slots in ascending order, in placement order.
+ * Inputs: load_hist i32 [P_total] (>= 0; the histogram of all ranks' tokens
+ * in a multi-GPU job), slot_expert_old i32 [P_total] (expert of each slot,
+ * -1 = empty).  Outputs: rep_count i32 [E], rep_slots i32 [E, R_max] (each
+ * expert's slots ascending, -1 padded; the table moe_forward takes with this
+ * R_max), slot_expert_new i32 [P_total].  Requires E <= P_total,
+ * P_total % n_ranks == 0 and E * R_max >= P_total; MOE_ERR_INVALID_ARG
+ * otherwise (nothing written). */
+int moe_eplb_rebalance(int32_t E, int32_t P_total, int32_t n_ranks, int32_t R_max, const int32_t* load_hist,
+                       const int32_t* slot_expert_old, int32_t* rep_count, int32_t* rep_slots,
+                       int32_t* slot_expert_new);
+
+/* EPLB weight migration for this GPU's slots [FlyDSL issue 978, Data-quality
+ * gates: "rebalancing and migrations actually occur"].  For each local slot s
+ * (s < dims->P_local) with src_expert[s] >= 0, the packed weights of slot s
+ * (pw1, pw1s, pw2, pw2s, layout of moe_pack_weights) become a byte copy of
+ * logical expert src_expert[s]'s packed weights in the pool; slots with -1
+ * keep their bytes.  The pool holds n_pool experts packed by moe_pack_weights
+ * (a pack with P_local = n_pool): on one GPU it stands in for the peer or
+ * host memory a multi-GPU job would fetch experts from.  src_expert: DEVICE
+ * i32 [P_local]; entries >= n_pool are skipped.  Only dims->H, F, P_local
+ * matter; the pool and the slots must not overlap.  Asynchronous on
+ * `stream`, one launch. */
+int moe_eplb_migrate(const moe_dims_t* dims, const int32_t* src_expert, int32_t n_pool, const uint8_t* pool_pw1,
+                     const uint8_t* pool_pw1s, const uint8_t* pool_pw2, const uint8_t* pool_pw2s, uint8_t* pw1,
+                     uint8_t* pw1s, uint8_t* pw2, uint8_t* pw2s, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_p
            "moe_pack_weights", "moe_route",
            "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
            "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
-           "moe_forward")
+           "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate")
 
 
 class MoeError(RuntimeError):
@@ -92,9 +92,11 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gemm2_combine_pairs.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_forward.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps),
                                   ctypes.POINTER(ctypes.c_int), P, ctypes.c_size_t, P]
-        for n in ("moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
+        L.moe_eplb_rebalance.argtypes = [I, I, I, I, P, P, P, P, P]
+        L.moe_eplb_migrate.argtypes = [D, P, I, P, P, P, P, P, P, P, P, P]
+        for n in ("moe_eplb_rebalance", "moe_eplb_migrate", "moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
                   "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
-                  "moe_forward"):
+                  "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate"):
             getattr(L, n).restype = I
         _lib_handle = L
     return _lib_handle
@@ -299,3 +301,47 @@ def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, 
         _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
     _check("moe_forward", rc)
     return PATH_NAMES[chosen.value]
+
+
+# ----------------------------------------------------------------------------
+# EPLB rebalance (host) and weight migration (device)
+# ----------------------------------------------------------------------------
+
+def _host_i32(a, name: str, n: int):
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        if a.device.type != "cpu":
+            raise ValueError(f"{name}: must be a host array")
+        a = a.numpy()
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    if a.size != n:
+        raise ValueError(f"{name}: {a.size} elements, expected {n}")
+    return a
+
+
+def moe_eplb_rebalance(E: int, P_total: int, n_ranks: int, R_max: int, load_hist, slot_expert_old):
+    """New replica table from recorded slot loads (host arrays in and out).
+    Returns numpy int32 (rep_count [E], rep_slots [E, R_max], slot_expert_new [P_total])."""
+    import numpy as np
+    h = _host_i32(load_hist, "load_hist", P_total)
+    old = _host_i32(slot_expert_old, "slot_expert_old", P_total)
+    rc = np.zeros(E, np.int32)
+    rs = np.zeros((E, R_max), np.int32)
+    new = np.zeros(P_total, np.int32)
+    c = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    st = lib().moe_eplb_rebalance(int(E), int(P_total), int(n_ranks), int(R_max), c(h), c(old), c(rc), c(rs), c(new))
+    _check("moe_eplb_rebalance", st)
+    return rc, rs, new
+
+
+def moe_eplb_migrate(d: Dims, src_expert, n_pool: int, pool, slots, stream=None):
+    """Copy pool experts into local slots: ``pool`` and ``slots`` are packed
+    weight tuples (pw1, pw1s, pw2, pw2s) over n_pool experts and d.P_local
+    slots; src_expert i32 [P_local] on the device (-1 = keep)."""
+    per = [moe_packed_bytes(d, i) // d.P_local for i in range(4)]
+    names = ("pw1", "pw1s", "pw2", "pw2s")
+    pp = [_ptr(t, "pool_" + n, u8, per[i] * n_pool) for i, (t, n) in enumerate(zip(pool, names))]
+    sp = [_ptr(t, n, u8, per[i] * d.P_local) for i, (t, n) in enumerate(zip(slots, names))]
+    rc = lib().moe_eplb_migrate(ctypes.byref(d), _ptr(src_expert, "src_expert", i32, d.P_local), int(n_pool),
+                                *pp, *sp, _stream(stream))
+    _check("moe_eplb_migrate", rc)

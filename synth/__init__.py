@@ -21,6 +21,9 @@ from .inputs import (  # noqa: F401
     make_sweep,
     make_custom,
     naive_replica_map,
+    expert_weights,
+    token_batch,
+    with_replica_map,
     skewed_logits,
     sha256,
 )

@@ -343,6 +343,43 @@ def skewed_logits(key: int, sub: int, T: int, E: int, k: int, s: float = 1.2) ->
     return _tokens(key, sub, T, 128, E, zipf_bias(pop, k))[0]
 
 
+def expert_weights(weights_key: int, H: int, F: int, experts,
+                   w_std: Tuple[float, float] = (W_STD, W_STD)):
+    """Natural MXFP4 weights of the listed logical experts, stacked in list
+    order: (w1 [n, 2F, H/2], w1s [n, 2F, H/32], w2 [n, H, F/2], w2s [n, H, F/32])."""
+    return _slot_weights(weights_key, H, F, np.asarray(list(experts), np.int32), tuple(w_std))
+
+
+def token_batch(key: int, sub: int, T: int, H: int, E: int, k: int, zipf_s: Optional[float] = None):
+    """One batch of router logits (f32 [T, E], Zipf-skewed if ``zipf_s``) and
+    activations (bf16 bits [T, H]); ``sub`` picks an independent draw."""
+    bias = None
+    if zipf_s is not None:
+        bias = zipf_bias(zipf_popularity(E, k, zipf_s, _rng(key, STREAM_EPLB, 0)), k)
+    return _tokens(key, sub, T, H, E, bias)
+
+
+def with_replica_map(wl: "Workload", rep_count, rep_slots, slot_expert_all, p0: int, P_local: int,
+                     weights_key: int, w_std: Tuple[float, float] = (W_STD, W_STD),
+                     logits: Optional[np.ndarray] = None, x: Optional[np.ndarray] = None,
+                     token_id_base: Optional[int] = None) -> "Workload":
+    """``wl`` with another replica table: slots [p0, p0 + P_local) of
+    ``slot_expert_all`` on this GPU, their weights drawn with ``weights_key``;
+    optionally another token batch."""
+    slot_expert_all = np.asarray(slot_expert_all, np.int32)
+    rep_slots = np.asarray(rep_slots, np.int32)
+    lg = wl.logits if logits is None else logits
+    xx = wl.x if x is None else x
+    base = wl.dims.token_id_base if token_id_base is None else token_id_base
+    d = wl.dims.replace(T=lg.shape[0], T_max=max(wl.dims.T_max, lg.shape[0]), P_total=len(slot_expert_all),
+                        p0=p0, P_local=P_local, R_max=rep_slots.shape[1], token_id_base=base)
+    se = slot_expert_all[p0:p0 + P_local].copy()
+    w1, w1s, w2, w2s = _slot_weights(weights_key, d.H, d.F, se, tuple(w_std))
+    return Workload(name=wl.name + f"_map{len(slot_expert_all)}", dims=d, logits=lg, x=xx,
+                    rep_count=np.asarray(rep_count, np.int32), rep_slots=rep_slots, slot_expert=se,
+                    w1=w1, w1s=w1s, w2=w2, w2s=w2s, popularity=wl.popularity)
+
+
 # ----------------------------------------------------------------------------
 # Public constructors
 # ----------------------------------------------------------------------------

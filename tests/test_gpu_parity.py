@@ -262,10 +262,10 @@ def test_quant_every_bf16_value():
 
 # ---------------------------------------------------------------------------- full size
 
-def _big_check(wl, n_slots=3, n_tokens=24, path="auto"):
+def _big_check(wl, n_slots=3, n_tokens=24, path="auto", buf=None):
     d = wl.dims
     _say(f"[case] {wl.name} T={d.T} path={path}")
-    res = P.run_forward(wl, path=path)
+    res = P.run_forward(wl, path=path, buf=buf)
     ref = P.oracle_front(wl)
     P.check_front(res, ref, d)
     rng = np.random.default_rng(d.T)
