@@ -267,8 +267,9 @@ int moe_eplb_rebalance(int32_t E, int32_t P_total, int32_t n_ranks, int32_t R_ma
                        const int32_t* slot_expert_old, int32_t* rep_count, int32_t* rep_slots,
                        int32_t* slot_expert_new);
 
-/* EPLB weight migration for this GPU's slots [FlyDSL issue 978, Data-quality
- * gates: "rebalancing and migrations actually occur"].  For each local slot s
+/* EPLB weight migration for this GPU's slots (the pages' data-quality gates
+ * check that rebalances and migrations take place [FlyDSL issue 978,
+ * Data-quality gates]).  For each local slot s
  * (s < dims->P_local) with src_expert[s] >= 0, the packed weights of slot s
  * (pw1, pw1s, pw2, pw2s, layout of moe_pack_weights) become a byte copy of
  * logical expert src_expert[s]'s packed weights in the pool; slots with -1
