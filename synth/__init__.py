@@ -22,6 +22,7 @@ from .inputs import (  # noqa: F401
     make_custom,
     naive_replica_map,
     expert_weights,
+    gate_weights,
     token_batch,
     with_replica_map,
     skewed_logits,

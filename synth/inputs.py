@@ -380,6 +380,17 @@ def with_replica_map(wl: "Workload", rep_count, rep_slots, slot_expert_all, p0: 
                     w1=w1, w1s=w1s, w2=w2, w2s=w2s, popularity=wl.popularity)
 
 
+STREAM_GATE = 5
+
+
+def gate_weights(key: int, E: int, H: int) -> np.ndarray:
+    """Router gate weights W_gate [E, H] as bf16 bits: N(0, 1/H) rounded to
+    bf16, so that the logits of N(0, 1) activations are close to N(0, 1) (the
+    logits the layer's workloads draw directly)."""
+    g = _rng(key, STREAM_GATE, 0)
+    return f32_to_bf16_bits(g.standard_normal((E, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H)))
+
+
 # ----------------------------------------------------------------------------
 # Public constructors
 # ----------------------------------------------------------------------------
