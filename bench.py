@@ -240,6 +240,41 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
         torch.cuda.empty_cache()
     if only is None or "eplb_migrate448" in only:
         eplb_migrate_point(steps, warmup)
+    for T in (512, 8192):
+        if only is None or f"router_T{T}" in only:
+            router_point(T, steps, warmup)
+
+
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
+
+
+def router_point(T: int, steps: int, warmup: int):
+    """Router projection (moe_router_logits) at the decode / prefill shares'
+    router shape: x bf16 [T, 7168] times a bf16 gate [384, 7168] -> f32
+    logits.  Algorithmic bytes: x, the gate and the logits once; flop 2 T E H."""
+    import numpy as np
+    import torch
+    import moe_expert_layer_sigmoid_amd as mx
+    import synth
+
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    H, E = 7168, 384
+    wl = synth.make_sweep(T, with_weights=False)
+    d = mx.Dims.of(wl.dims)
+    x = torch.from_numpy(wl.x.view("int16")).to(dev)
+    wg = torch.from_numpy(synth.gate_weights(1, E, H).view(np.int16)).to(dev)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ws = mx.router_workspace(d)
+    ms = _time(lambda i: mx.moe_router_logits(d, x, wg, lg, ws, stream=st), steps, warmup, st)
+    nbytes = T * H * 2 + E * H * 2 + T * E * 4
+    flops = 2 * T * E * H
+    t = ms * 1e-3
+    hbm, mfma = nbytes / t / 1e9 / HBM_PEAK_GBS, flops / t / 1e12 / BF16_PEAK_TFLOPS
+    rec = {"point": f"router_T{T}", "T": T, "H": H, "E": E, "ms": round(ms, 4),
+           "tokens_per_s": round(T / t, 1), "hbm_frac": round(hbm, 4), "mfma_bf16_frac": round(mfma, 4),
+           "roofline_frac": round(max(hbm, mfma), 4), "bound": "hbm" if hbm >= mfma else "mfma"}
+    print(json.dumps(rec), flush=True)
 
 
 def eplb_migrate_point(steps: int, warmup: int):

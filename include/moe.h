@@ -237,6 +237,20 @@ int moe_forward(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, cons
                 uint16_t* out, const moe_taps_t* taps, moe_path_t* chosen,
                 void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* Router projection in front of a1: logits[t][e] = sum_k x[t][k] w_gate[e][k]
+ * (bf16 x bf16 products, f32 accumulation in an unspecified order).  The
+ * gate is stored in BF16 [InferenceX PR 3430, Additional detail section];
+ * routing then takes the top-k of these logits (moe_route / moe_forward).
+ * Layouts: x bf16 [T, H] (as everywhere), w_gate bf16 [E, H] (one row per
+ * logical expert, no bias), logits f32 [T, E].  Only dims->T, T_max, H, E
+ * matter (the other fields must still be valid dims).  Workspace: at least
+ * moe_router_workspace_bytes(dims) bytes, 256-byte aligned (split-K partial
+ * sums; sized by T_max).  T == 0 launches nothing.  Asynchronous on `stream`;
+ * one or two launches. */
+size_t moe_router_workspace_bytes(const moe_dims_t* dims);
+int moe_router_logits(const moe_dims_t* dims, const uint16_t* x, const uint16_t* w_gate, float* logits,
+                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
 /* EPLB rebalance: a new replica table from the loads recorded by a2 (host
  * call; every pointer is a HOST pointer; no stream, no device memory).
  * The pages run EPLB with redundant physical experts and rebalance every few

@@ -28,7 +28,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_p
            "moe_pack_weights", "moe_route",
            "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
            "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
-           "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate")
+           "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
+           "moe_router_workspace_bytes", "moe_router_logits")
 
 
 class MoeError(RuntimeError):
@@ -92,11 +93,16 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gemm2_combine_pairs.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_forward.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps),
                                   ctypes.POINTER(ctypes.c_int), P, ctypes.c_size_t, P]
+        L.moe_router_workspace_bytes.argtypes = [D]
+        L.moe_router_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_router_logits.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_router_logits.restype = I
         L.moe_eplb_rebalance.argtypes = [I, I, I, I, P, P, P, P, P]
         L.moe_eplb_migrate.argtypes = [D, P, I, P, P, P, P, P, P, P, P, P]
         for n in ("moe_eplb_rebalance", "moe_eplb_migrate", "moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
                   "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
-                  "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate"):
+                  "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
+           "moe_router_workspace_bytes", "moe_router_logits"):
             getattr(L, n).restype = I
         _lib_handle = L
     return _lib_handle
@@ -345,3 +351,24 @@ def moe_eplb_migrate(d: Dims, src_expert, n_pool: int, pool, slots, stream=None)
     rc = lib().moe_eplb_migrate(ctypes.byref(d), _ptr(src_expert, "src_expert", i32, d.P_local), int(n_pool),
                                 *pp, *sp, _stream(stream))
     _check("moe_eplb_migrate", rc)
+
+
+# ----------------------------------------------------------------------------
+# Router projection
+# ----------------------------------------------------------------------------
+
+def moe_router_workspace_bytes(d: Dims) -> int:
+    return int(lib().moe_router_workspace_bytes(ctypes.byref(d)))
+
+
+def router_workspace(d: Dims, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_router_workspace_bytes(d), 256), dtype=u8, device=device)
+
+
+def moe_router_logits(d: Dims, x, w_gate, logits, ws, stream=None):
+    """logits f32 [T, E] = x bf16 [T, H] (int16 bits or bfloat16) times w_gate bf16 [E, H] transposed."""
+    rc = lib().moe_router_logits(ctypes.byref(d), _ptr(x, "x", _bf16(x), d.T * d.H),
+                                 _ptr(w_gate, "w_gate", _bf16(w_gate), d.E * d.H),
+                                 _ptr(logits, "logits", f32, d.T * d.E), _ptr(ws, "workspace", u8), ws.numel(),
+                                 _stream(stream))
+    _check("moe_router_logits", rc)

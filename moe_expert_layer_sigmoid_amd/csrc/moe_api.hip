@@ -374,4 +374,22 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
   return MOE_OK;
 }
 
+size_t moe_router_workspace_bytes(const moe_dims_t* d) {
+  if (check_dims(d) != MOE_OK) return 0;
+  return round_up(router_partial_bytes(d->T_max, d->E, d->H), kAlign);
+}
+
+int moe_router_logits(const moe_dims_t* d, const uint16_t* x, const uint16_t* w_gate, float* logits, void* ws,
+                      size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc != MOE_OK) return rc;
+  if (!dev_ok(x) || !dev_ok(w_gate) || !dev_ok(logits)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_router_workspace_bytes(d);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws % kAlign) != 0) return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(launch_router(x, w_gate, logits, static_cast<float*>(ws), d->T, d->E, d->H, st));
+}
+
 }  // extern "C"

@@ -80,4 +80,23 @@ hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_
 hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                               const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
 
+// Router projection (kernels_router.hip): logits [T, E] f32 = x [T, H] bf16 times
+// w_gate [E, H] bf16 transposed.  Plan: blocks of 128 experts x 16 ni tokens
+// (ni = 8 from kRouterLargeT tokens, 4 from kRouterMidT, else 1); the K range is
+// split over `splits` blocks until the grid has kRouterMinBlocks blocks (at most
+// kRouterMaxSplits, each split at least 128 columns), the partial sums going to
+// `partial` [splits, T, E] and a reduce kernel adding them in split order.
+constexpr int kRouterLargeT = 4096;
+constexpr int kRouterMidT = 1024;
+constexpr int kRouterMinBlocks = 256;
+constexpr int kRouterMaxSplits = 16;
+struct RouterPlan {
+  int ni, gx, gy, splits, klen;
+};
+RouterPlan router_plan(int T, int E, int H);
+// Bytes of `partial` any T <= T_max needs (an upper bound).
+size_t router_partial_bytes(int T_max, int E, int H);
+hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, float* partial, int T, int E, int H,
+                         hipStream_t st);
+
 }  // namespace moe
