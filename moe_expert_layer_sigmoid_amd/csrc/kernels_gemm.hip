@@ -107,6 +107,8 @@ struct SOps {
   uint32_t wt[4];          // tile * data_tile + 16 * lane
   uint32_t wst[4];         // tile * scale_tile + 8 * lane
   uint32_t xlo[NT];        // per token tile: token row * K + 16 g (past the buffer: zeros)
+  uint32_t kx;             // K of the token rows (bytes)
+  uint32_t lim;            // the token buffer's size: offsets from here read zeros
   const uint8_t* sxs[NT];  // LDS: this lane's token's 128-column scales (zero-padded)
 };
 
@@ -126,13 +128,21 @@ __device__ __forceinline__ void s_load(SStage<NT>& S, const SOps<NT>& O, int st,
     S.a[rt][0] = buf_load16_p<WAUX>(O.w, O.wt[rt], wo);
     S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wt[rt] + 1024, wo);
   }
+  // Steps past K (the packed weights pad K to a multiple of 1024) take zero
+  // tokens, not the bytes after the row: those may belong to rows nothing
+  // wrote (pair rows of remote pairs) and hold fp8 NaN codes, which a zero
+  // weight would not cancel.  Each 128-column half-step is whole (K is a
+  // multiple of 128), so the test is uniform.
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int i = 0; i < 2; ++i) {
+    const bool live = xo + (uint32_t)i * 128 < O.kx;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      S.b[n][i].h[0] = buf_load16(O.x, O.xlo[n] + i * 128, xo);
-      S.b[n][i].h[1] = buf_load16(O.x, O.xlo[n] + 64 + i * 128, xo);
+    for (int n = 0; n < NT; ++n) {
+      const uint32_t b = live ? O.xlo[n] : O.lim;
+      S.b[n][i].h[0] = buf_load16(O.x, b + i * 128, xo);
+      S.b[n][i].h[1] = buf_load16(O.x, b + 64 + i * 128, xo);
     }
+  }
 }
 
 struct SScales {
@@ -353,6 +363,8 @@ __device__ __forceinline__ void token_operand(SOps<NT>& O, const uint8_t* x, con
                                               int nrow, int nsrc, int K, int l16, int g) {
   const uint32_t lim = PAIRS ? (uint32_t)nsrc * (uint32_t)K : (uint32_t)nrow * (uint32_t)K;
   O.x = PAIRS ? make_rsrc(x, lim) : make_rsrc(x + (size_t)(R.row0 + tt0) * K, lim);
+  O.kx = (uint32_t)K;
+  O.lim = lim;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int r = n * 16 + l16;
