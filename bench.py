@@ -243,6 +243,57 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
     for T in (512, 8192):
         if only is None or f"router_T{T}" in only:
             router_point(T, steps, warmup)
+    if only is None or "graph_T512" in only:
+        graph_point(steps, warmup)
+
+
+def graph_point(steps: int, warmup: int):
+    """The decode share (512 tokens) as one captured HIP graph of the
+    device-count small-input call (moe_forward_small_m, bucket 512): replay
+    time with all 512 tokens valid and for an idle step (0 valid), next to
+    the eager moe_forward, weights rotated over 3 copies in both."""
+    import torch
+    import moe_expert_layer_sigmoid_amd as mx
+    import synth
+
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    wl = synth.make("decode512")
+    d = mx.Dims.of(wl.dims)
+    nat = [torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
+    w = [mx.pack_weights(d, *nat)]
+    del nat
+    for _ in range(2):
+        w.append(tuple(t.clone() for t in w[0]))
+    x = torch.from_numpy(wl.x.view("int16")).to(dev)
+    logits = torch.from_numpy(wl.logits).to(dev)
+    rc = torch.from_numpy(wl.rep_count).to(dev)
+    rs = torch.from_numpy(wl.rep_slots).to(dev)
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
+    ws = mx.workspace(d)
+    nt = torch.tensor([d.T], dtype=torch.int32, device=dev)
+    eager = _time(lambda i: mx.moe_forward(d, x, logits, *w[i % 3], rc, rs, out, ws, path="small_m"), steps,
+                  warmup, st)
+    side = torch.cuda.Stream()
+    side.wait_stream(st)
+    with torch.cuda.stream(side):
+        for i in range(3):
+            mx.moe_forward_small_m(d, nt, x, logits, *w[i], rc, rs, out, ws)
+    st.wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            mx.moe_forward_small_m(d, nt, x, logits, *w[i], rc, rs, out, ws)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    full = _time(lambda i: graphs[i % 3].replay(), steps, warmup, st)
+    nt.fill_(0)
+    idle = _time(lambda i: graphs[i % 3].replay(), steps, warmup, st)
+    rec = {"point": "graph_T512", "T": d.T, "eager_ms": round(eager, 4), "graph_ms": round(full, 4),
+           "graph_idle_ms": round(idle, 4), "tokens_per_s_graph": round(d.T / (full * 1e-3), 1)}
+    print(json.dumps(rec), flush=True)
 
 
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published

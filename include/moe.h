@@ -237,6 +237,25 @@ int moe_forward(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, cons
                 uint16_t* out, const moe_taps_t* taps, moe_path_t* chosen,
                 void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* The small-input path with the token count on the device, for captured
+ * graphs: decode graphs are captured per token-count bucket and must also
+ * run idle (zero-token) steps [sglang PR 35619, Summary: graph-safe idle
+ * handling; sglang PR 47065, Modifications: DP-synchronised buckets for the
+ * captured graphs, forward_small_m(max_tokens=)].  dims->T is the bucket
+ * capacity (<= 1024; every launch shape follows it); num_tokens (DEVICE, i32,
+ * 4-byte aligned) holds the step's valid count n, read by the kernels, so one
+ * capture serves every n in [0, dims->T] (values outside are clamped).  The
+ * first n tokens go through the layer exactly as moe_forward(MOE_PATH_SMALL_M)
+ * with T = n computes them; rows [n, T) of `out` are written as +0; load_hist
+ * (nullable) counts only the first n tokens' pairs; taps hold the first n
+ * tokens' intermediates (phys_ids of the others = -1, the rest unspecified).
+ * Other arguments and errors as moe_forward.  Launches no memset and
+ * allocates nothing, so the four launches can be captured into a graph. */
+int moe_forward_small_m(const moe_dims_t* dims, const int32_t* num_tokens, const uint16_t* x, const float* logits,
+                        const uint8_t* pw1, const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s,
+                        const int32_t* rep_count, const int32_t* rep_slots, int32_t* load_hist, uint16_t* out,
+                        const moe_taps_t* taps, void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
 /* Router projection in front of a1: logits[t][e] = sum_k x[t][k] w_gate[e][k]
  * (bf16 x bf16 products, f32 accumulation in an unspecified order).  The
  * gate is stored in BF16 [InferenceX PR 3430, Additional detail section];

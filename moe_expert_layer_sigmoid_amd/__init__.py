@@ -29,7 +29,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_p
            "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
            "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
            "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
-           "moe_router_workspace_bytes", "moe_router_logits")
+           "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m")
 
 
 class MoeError(RuntimeError):
@@ -93,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gemm2_combine_pairs.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_forward.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps),
                                   ctypes.POINTER(ctypes.c_int), P, ctypes.c_size_t, P]
+        L.moe_forward_small_m.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps), P,
+                                          ctypes.c_size_t, P]
+        L.moe_forward_small_m.restype = I
         L.moe_router_workspace_bytes.argtypes = [D]
         L.moe_router_workspace_bytes.restype = ctypes.c_size_t
         L.moe_router_logits.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
@@ -102,7 +105,7 @@ def lib() -> ctypes.CDLL:
         for n in ("moe_eplb_rebalance", "moe_eplb_migrate", "moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
                   "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
                   "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
-           "moe_router_workspace_bytes", "moe_router_logits"):
+           "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m"):
             getattr(L, n).restype = I
         _lib_handle = L
     return _lib_handle
@@ -307,6 +310,29 @@ def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, 
         _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
     _check("moe_forward", rc)
     return PATH_NAMES[chosen.value]
+
+
+def moe_forward_small_m(d: Dims, num_tokens, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, out, ws,
+                        load_hist=None, taps: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> None:
+    """The small-input path with the valid token count read on the device
+    from ``num_tokens`` (int32 device tensor, one element); d.T is the bucket
+    capacity.  Allocates nothing: safe inside torch.cuda.graph capture."""
+    TK, _ = _sizes(d)
+    tp = None
+    if taps is not None:
+        need = dict(topk_ids=(i32, TK), topk_w=(f32, TK), phys_ids=(i32, TK), counts=(i32, d.P_local),
+                    offsets=(i32, d.P_local + 1), xq_tok=(u8, d.T * d.H), xs_tok=(u8, d.T * (d.H // 128)),
+                    aq_pair=(u8, TK * d.F), as_pair=(u8, TK * (d.F // 128)))
+        tp = Taps(**{n: _ptr(taps.get(n), n, *need[n]) for n in need})
+    rc = lib().moe_forward_small_m(
+        ctypes.byref(d), _ptr(num_tokens, "num_tokens", i32, 1), _ptr(x, "x", _bf16(x), d.T * d.H),
+        _ptr(logits, "logits", f32, d.T * d.E),
+        _ptr(pw1, "pw1", u8, moe_packed_bytes(d, 0)), _ptr(pw1s, "pw1s", u8, moe_packed_bytes(d, 1)),
+        _ptr(pw2, "pw2", u8, moe_packed_bytes(d, 2)), _ptr(pw2s, "pw2s", u8, moe_packed_bytes(d, 3)),
+        _ptr(rep_count, "rep_count", i32, d.E), _ptr(rep_slots, "rep_slots", i32, d.E * d.R_max),
+        _ptr(load_hist, "load_hist", i32, d.P_total), _ptr(out, "out", _bf16(out), d.T * d.H),
+        ctypes.byref(tp) if tp is not None else None, _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
+    _check("moe_forward_small_m", rc)
 
 
 # ----------------------------------------------------------------------------

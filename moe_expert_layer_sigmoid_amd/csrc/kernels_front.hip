@@ -495,14 +495,21 @@ hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* ro
 constexpr int kFrontThreads = 1024;
 constexpr int kRepLds = 4096;  // replica-table entries staged in LDS
 
+//
+// With a device token count (t_dev != NULL) the grid covers the capacity T
+// and only the first min(*t_dev, T) tokens are valid: the pairs of the other
+// tokens get phys = -1 (no slot), so the GEMMs list none of them, the combine
+// writes +0 rows for them and the load record skips them.
 template <int EPL>
 __global__ __launch_bounds__(kFrontThreads) void k_front(
     int T, int E, int k, int H, const float* __restrict__ logits, const uint16_t* __restrict__ x,
     const int32_t* __restrict__ rep_count, const int32_t* __restrict__ rep_slots, int R_max,
     uint32_t token_id_base, int P_total, int nr, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ phys, int32_t* __restrict__ partial, uint8_t* __restrict__ xq_tok,
-    uint8_t* __restrict__ xs_tok) {
+    uint8_t* __restrict__ xs_tok, const int32_t* __restrict__ t_dev) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Tcap = T;
+  if (t_dev) T = __builtin_amdgcn_readfirstlane(min(max(*t_dev, 0), Tcap));
   if ((int)blockIdx.x < nr) {
     __shared__ int s_rc[1024];
     __shared__ int s_rs[kRepLds];
@@ -526,6 +533,8 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(
       ids[pr] = id;
       w[pr] = wt;
       phys[pr] = p;
+    } else if (t < Tcap && lane < k) {
+      phys[(size_t)t * k + lane] = -1;  // past the device token count: no slot
     }
     if (lane < k) s_phys[wave * k + lane] = p;
     __syncthreads();
@@ -556,7 +565,7 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(
 hipError_t launch_front(int T, int E, int k, int H, const float* logits, const uint16_t* x, const int32_t* rep_count,
                         const int32_t* rep_slots, int R_max, uint32_t token_id_base, int P_total, int32_t* ids,
                         float* w, int32_t* phys, int32_t* partial, uint8_t* xq_tok, uint8_t* xs_tok,
-                        hipStream_t st) {
+                        hipStream_t st, const int32_t* t_dev) {
   if (T == 0) return hipSuccess;
   const int nr = (T + 15) / 16;
   const long waves = (long)T * ((H / kActBlock + 3) / 4);
@@ -566,7 +575,7 @@ hipError_t launch_front(int T, int E, int k, int H, const float* logits, const u
   case N:                                                                                                      \
     k_front<N><<<grid, kFrontThreads, 0, st>>>(T, E, k, H, logits, x, rep_count, rep_slots, R_max,             \
                                                token_id_base, P_total, nr, ids, w, phys, partial, xq_tok,     \
-                                               xs_tok);                                                       \
+                                               xs_tok, t_dev);                                                \
     break;
     MOE_ROUTE_CASES(X)
 #undef X

@@ -298,10 +298,16 @@ int moe_grouped_gemm2_combine_pairs(const moe_dims_t* d, const uint8_t* aq_pair,
   return MOE_OK;
 }
 
-int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const float* logits, const uint8_t* pw1,
-                const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rep_count,
-                const int32_t* rep_slots, int32_t* load_hist, uint16_t* out, const moe_taps_t* taps,
-                moe_path_t* chosen, void* ws, size_t ws_bytes, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward; t_dev (device, nullable) = the device token count of
+// moe_forward_small_m (SMALL_M only).
+int forward_impl(const moe_dims_t* d, moe_path_t path, const int32_t* t_dev, const uint16_t* x, const float* logits,
+                 const uint8_t* pw1, const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s,
+                 const int32_t* rep_count, const int32_t* rep_slots, int32_t* load_hist, uint16_t* out,
+                 const moe_taps_t* taps, moe_path_t* chosen, void* ws, size_t ws_bytes, moe_stream_t stream) {
   int rc = check_dims(d);
   if (rc) return rc;
   if (path < MOE_PATH_AUTO || path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
@@ -352,7 +358,7 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
     uint8_t* aq_p = pick(tp.aq_pair, L.aq);
     uint8_t* as_p = pick(tp.as_pair, L.as);
     MOE_TRY(launch_front(d->T, d->E, d->k, d->H, logits, x, rep_count, rep_slots, d->R_max, d->token_id_base,
-                         d->P_total, ids, w, phys, partial, xq_tok, xs_tok, st));
+                         d->P_total, ids, w, phys, partial, xq_tok, xs_tok, st, t_dev));
     const int nt = stream_tiles(d);
     MOE_TRY(launch_gemm1_pairs(xq_tok, xs_tok, phys, d->T, d->k, d->p0, pw1, pw1s, aq_p, as_p, counts, d->H, d->F,
                                d->P_local, nt, st));
@@ -372,6 +378,27 @@ int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const f
   MOE_TRY(gemm2(p, aq, as, offsets, pw2, pw2s, y, d, st));
   MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, st));
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const float* logits, const uint8_t* pw1,
+                const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rep_count,
+                const int32_t* rep_slots, int32_t* load_hist, uint16_t* out, const moe_taps_t* taps,
+                moe_path_t* chosen, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return forward_impl(d, path, nullptr, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, load_hist, out, taps,
+                      chosen, ws, ws_bytes, stream);
+}
+
+int moe_forward_small_m(const moe_dims_t* d, const int32_t* num_tokens, const uint16_t* x, const float* logits,
+                        const uint8_t* pw1, const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s,
+                        const int32_t* rep_count, const int32_t* rep_slots, int32_t* load_hist, uint16_t* out,
+                        const moe_taps_t* taps, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (!num_tokens || ((uintptr_t)num_tokens & 3u)) return MOE_ERR_INVALID_ARG;
+  return forward_impl(d, MOE_PATH_SMALL_M, num_tokens, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots,
+                      load_hist, out, taps, nullptr, ws, ws_bytes, stream);
 }
 
 size_t moe_router_workspace_bytes(const moe_dims_t* d) {

@@ -33,11 +33,13 @@ hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* ro
 
 // Small-M path (pair-indexed rows).  Front: routing, remap, per-16-token
 // chunk counts partial[ceil(T/16), P_total], and every token quantised into
-// xq_tok [T, H] / xs_tok [T, H/128].
+// xq_tok [T, H] / xs_tok [T, H/128].  t_dev (nullable, device): a token count
+// read on the device; tokens from min(*t_dev, T) on get phys = -1 (idle).
 constexpr int kFrontTokens = 16;
 hipError_t launch_front(int T, int E, int k, int H, const float* logits, const uint16_t* x, const int32_t* rep_count,
                         const int32_t* rep_slots, int R_max, uint32_t token_id_base, int P_total, int32_t* ids,
-                        float* w, int32_t* phys, int32_t* partial, uint8_t* xq_tok, uint8_t* xs_tok, hipStream_t st);
+                        float* w, int32_t* phys, int32_t* partial, uint8_t* xq_tok, uint8_t* xs_tok, hipStream_t st,
+                        const int32_t* t_dev = nullptr);
 // Combine of pair rows y [T*k, H], plus load_hist += the front's chunk
 // counts (load_hist nullable) and offsets from the per-slot counts GEMM1 wrote.
 hipError_t launch_combine_pairs(int T, int H, int k, const float* y, const int32_t* phys, int p0, int P_local,

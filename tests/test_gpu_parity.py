@@ -308,3 +308,24 @@ def test_skewed_routing_with_eplb_8192_tokens():
     res = _big_check(wl)
     # the recorder saw every pair, on all 448 physical slots
     assert res["hist"].sum() == wl.dims.T * wl.dims.k and wl.dims.P_total == 448
+
+
+@pytest.mark.parametrize("path", ["small_m", "staged"])
+def test_padded_k_ignores_workspace_bytes(path):
+    """d_model 512 and d_ff 256 pad K to 1024 in the packed weights: the
+    padded steps must read zero tokens, whatever the workspace holds (here
+    every byte 0x7F, an fp8 NaN code) -- a regression case."""
+    wl = synth.make_custom(T=64, H=512, F=256, E=384, k=6, P_local=48, seed=410)
+    d = mx.Dims.of(wl.dims)
+    _say(f"[case] padded K, workspace of NaN codes, path={path}")
+    buf = P.upload(wl)
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device="cuda")
+    ws = torch.full((mx.moe_workspace_bytes(d),), 0x7F, dtype=torch.uint8, device="cuda")
+    mx.moe_forward(d, buf["x"], buf["logits"], buf["w1"], buf["w1s"], buf["w2"], buf["w2s"], buf["rep_count"],
+                   buf["rep_slots"], out, ws, path=path)
+    torch.cuda.synchronize()
+    got = fm.bf16_to_f64(out.cpu().numpy().view(np.uint16))
+    assert np.all(np.isfinite(got))
+    n2, _ = P.rel_errors(got, om.forward(wl)["out"])
+    assert n2 <= P.OUT_NORM_TOL, n2
+    _say(f"   ok: normwise {n2:.2e}")
