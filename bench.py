@@ -245,6 +245,39 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
             router_point(T, steps, warmup)
     if only is None or "graph_T512" in only:
         graph_point(steps, warmup)
+    if only is None or "a16w4_T512" in only:
+        a16w4_point(steps, warmup)
+
+
+def a16w4_point(steps: int, warmup: int):
+    """The a16w4 variant (bf16 activations on the MXFP4 experts) at the decode
+    share's shapes, weights rotated over 3 copies: tokens/s and the fraction of
+    the layer's HBM roofline (the same algorithmic bytes as the a8w4 layer)."""
+    import torch
+    import moe_expert_layer_sigmoid_amd as mx
+    import synth
+
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    wl = synth.make("decode512")
+    d = mx.Dims.of(wl.dims)
+    nat = [torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
+    w = [mx.pack_weights(d, *nat)]
+    del nat
+    for _ in range(2):
+        w.append(tuple(t.clone() for t in w[0]))
+    x = torch.from_numpy(wl.x.view("int16")).to(dev)
+    logits = torch.from_numpy(wl.logits).to(dev)
+    rc = torch.from_numpy(wl.rep_count).to(dev)
+    rs = torch.from_numpy(wl.rep_slots).to(dev)
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
+    ws = mx.a16w4_workspace(d)
+    ms = _time(lambda i: mx.moe_forward_a16w4(d, x, logits, *w[i % 3], rc, rs, out, ws), steps, warmup, st)
+    touched = 48
+    lay = layer_bytes(d, touched)
+    rec = {"point": "a16w4_T512", "T": d.T, "ms_per_step": round(ms, 4), "tokens_per_s": round(d.T / (ms * 1e-3), 1),
+           "hbm_frac": round(lay / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    print(json.dumps(rec), flush=True)
 
 
 def graph_point(steps: int, warmup: int):

@@ -237,6 +237,26 @@ int moe_forward(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, cons
                 uint16_t* out, const moe_taps_t* taps, moe_path_t* chosen,
                 void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* a16w4 variant of the whole layer: bf16 activations on the MXFP4 experts,
+ * no activation quantisation (the pages' non-EP arms run the MXFP4 experts
+ * with bf16 activations [InferenceX PR 3430, Additional detail section]).
+ * Routing, remap + record and buckets as moe_forward; GEMM1 takes each
+ * bucketed row's bf16 input row as is (products exact, f32 accumulation),
+ * act = silu(gate) * up rounded to bf16 (nearest even), GEMM2 on the bf16
+ * act, combine as moe_forward.  The weight scale bytes of non-zero MXFP4
+ * elements must lie in [2, 252] (every value then a normal bf16; the caller's
+ * contract like finite inputs).  taps (nullable): topk_ids, topk_w, phys_ids,
+ * counts, offsets, row_of_pair, pair_of_row as moe_forward (other members
+ * ignored); act_tap (nullable, device): bf16 act rows [T_max*k, F] in bucket
+ * order.  Workspace: moe_a16w4_workspace_bytes(dims).  T * H * 2 and
+ * T_max * k * F * 2 bytes must stay below 2^31 (else MOE_ERR_UNSUPPORTED).
+ * Seven launches on `stream`. */
+size_t moe_a16w4_workspace_bytes(const moe_dims_t* dims);
+int moe_forward_a16w4(const moe_dims_t* dims, const uint16_t* x, const float* logits, const uint8_t* pw1,
+                      const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rep_count,
+                      const int32_t* rep_slots, int32_t* load_hist, uint16_t* out, const moe_taps_t* taps,
+                      uint16_t* act_tap, void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
 /* The small-input path with the token count on the device, for captured
  * graphs: decode graphs are captured per token-count bucket and must also
  * run idle (zero-token) steps [sglang PR 35619, Summary: graph-safe idle

@@ -29,7 +29,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_p
            "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
            "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
            "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
-           "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m")
+           "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m",
+           "moe_a16w4_workspace_bytes", "moe_forward_a16w4")
 
 
 class MoeError(RuntimeError):
@@ -96,6 +97,11 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_small_m.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps), P,
                                           ctypes.c_size_t, P]
         L.moe_forward_small_m.restype = I
+        L.moe_a16w4_workspace_bytes.argtypes = [D]
+        L.moe_a16w4_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_forward_a16w4.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps), P, P,
+                                        ctypes.c_size_t, P]
+        L.moe_forward_a16w4.restype = I
         L.moe_router_workspace_bytes.argtypes = [D]
         L.moe_router_workspace_bytes.restype = ctypes.c_size_t
         L.moe_router_logits.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
@@ -105,7 +111,8 @@ def lib() -> ctypes.CDLL:
         for n in ("moe_eplb_rebalance", "moe_eplb_migrate", "moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
                   "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
                   "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
-           "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m"):
+           "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m",
+           "moe_a16w4_workspace_bytes", "moe_forward_a16w4"):
             getattr(L, n).restype = I
         _lib_handle = L
     return _lib_handle
@@ -398,3 +405,37 @@ def moe_router_logits(d: Dims, x, w_gate, logits, ws, stream=None):
                                  _ptr(logits, "logits", f32, d.T * d.E), _ptr(ws, "workspace", u8), ws.numel(),
                                  _stream(stream))
     _check("moe_router_logits", rc)
+
+
+# ----------------------------------------------------------------------------
+# a16w4 variant
+# ----------------------------------------------------------------------------
+
+def moe_a16w4_workspace_bytes(d: Dims) -> int:
+    return int(lib().moe_a16w4_workspace_bytes(ctypes.byref(d)))
+
+
+def a16w4_workspace(d: Dims, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_a16w4_workspace_bytes(d), 256), dtype=u8, device=device)
+
+
+def moe_forward_a16w4(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, out, ws, load_hist=None,
+                      taps: Optional[Dict[str, torch.Tensor]] = None, act=None, stream=None) -> None:
+    """The layer with bf16 activations on the packed MXFP4 experts.  ``act``
+    (optional, bf16 [T_max*k, F] as int16 bits) receives the GEMM1 act rows."""
+    TK, TMK = _sizes(d)
+    tp = None
+    if taps is not None:
+        need = dict(topk_ids=(i32, TK), topk_w=(f32, TK), phys_ids=(i32, TK), counts=(i32, d.P_local),
+                    offsets=(i32, d.P_local + 1), row_of_pair=(i32, TK), pair_of_row=(i32, TMK))
+        tp = Taps(**{n: _ptr(taps.get(n), n, *need[n]) for n in need})
+    rc = lib().moe_forward_a16w4(
+        ctypes.byref(d), _ptr(x, "x", _bf16(x), d.T * d.H), _ptr(logits, "logits", f32, d.T * d.E),
+        _ptr(pw1, "pw1", u8, moe_packed_bytes(d, 0)), _ptr(pw1s, "pw1s", u8, moe_packed_bytes(d, 1)),
+        _ptr(pw2, "pw2", u8, moe_packed_bytes(d, 2)), _ptr(pw2s, "pw2s", u8, moe_packed_bytes(d, 3)),
+        _ptr(rep_count, "rep_count", i32, d.E), _ptr(rep_slots, "rep_slots", i32, d.E * d.R_max),
+        _ptr(load_hist, "load_hist", i32, d.P_total), _ptr(out, "out", _bf16(out), d.T * d.H),
+        ctypes.byref(tp) if tp is not None else None,
+        _ptr(act, "act", _bf16(act), TMK * d.F) if act is not None else None,
+        _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
+    _check("moe_forward_a16w4", rc)

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["moe_api.hip", "kernels_front.hip", "kernels_gemm.hip", "kernels_tiled.hip", "eplb.hip",
-           "kernels_router.hip"]
+           "kernels_router.hip", "kernels_a16.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -419,4 +419,64 @@ int moe_router_logits(const moe_dims_t* d, const uint16_t* x, const uint16_t* w_
   return hip_status(launch_router(x, w_gate, logits, static_cast<float*>(ws), d->T, d->E, d->H, st));
 }
 
+size_t moe_a16w4_workspace_bytes(const moe_dims_t* d) {
+  if (check_dims(d) != MOE_OK) return 0;
+  return layout_of(d).total + round_up((size_t)d->T_max * d->k * d->F * 2, kAlign);
+}
+
+int moe_forward_a16w4(const moe_dims_t* d, const uint16_t* x, const float* logits, const uint8_t* pw1,
+                      const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rep_count,
+                      const int32_t* rep_slots, int32_t* load_hist, uint16_t* out, const moe_taps_t* taps,
+                      uint16_t* act_tap, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dev_ok(x) || !dev_ok(logits) || !dev_ok(pw1) || !dev_ok(pw1s) || !dev_ok(pw2) || !dev_ok(pw2s) ||
+      !dev_ok(rep_count) || !dev_ok(rep_slots) || !opt_ok(load_hist) || !dev_ok(out) || !opt_ok(act_tap))
+    return MOE_ERR_INVALID_ARG;
+  if (taps) {
+    const void* tp[] = {taps->topk_ids, taps->topk_w, taps->phys_ids, taps->counts, taps->offsets,
+                        taps->row_of_pair, taps->pair_of_row};
+    for (const void* p : tp)
+      if (!opt_ok(p)) return MOE_ERR_INVALID_ARG;
+  }
+  const size_t need = moe_a16w4_workspace_bytes(d);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws % kAlign) != 0) return MOE_ERR_INVALID_ARG;
+  if ((size_t)d->T_max * d->H * 2 >= (1u << 31) || (size_t)d->T_max * d->k * d->F * 2 >= (1u << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (d->T == 0) return MOE_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  Layout L = layout_of(d);
+  auto pick = [&](auto* tap, size_t off) -> decltype(tap) {
+    return tap ? tap : reinterpret_cast<decltype(tap)>(static_cast<char*>(ws) + off);
+  };
+  const moe_taps_t none{};
+  const moe_taps_t& tp = taps ? *taps : none;
+  int32_t* ids = pick(tp.topk_ids, L.ids);
+  float* w = pick(tp.topk_w, L.w);
+  int32_t* phys = pick(tp.phys_ids, L.phys);
+  int32_t* counts = pick(tp.counts, L.counts);
+  int32_t* offsets = pick(tp.offsets, L.offsets);
+  int32_t* rop = pick(tp.row_of_pair, L.rop);
+  int32_t* por = pick(tp.pair_of_row, L.por);
+  uint16_t* act = act_tap ? act_tap : at<uint16_t>(ws, L.total);
+  int32_t* rank = at<int32_t>(ws, L.rank);
+  int32_t* partial = at<int32_t>(ws, L.partial);
+  int32_t* base = at<int32_t>(ws, L.base);
+  float* y = at<float>(ws, L.y);
+  // routing, remap + record, buckets as in the a8w4 layer; the row maps come
+  // from the bucketed quantise kernel (its fp8 rows are not used here)
+  MOE_TRY(launch_route(logits, d->T, d->E, d->k, ids, w, st));
+  MOE_TRY(launch_count(d->T, d->k, ids, rep_count, rep_slots, d->R_max, d->token_id_base, phys, true, d->P_total,
+                       d->p0, d->P_local, partial, rank, st));
+  MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, counts, offsets, base, load_hist, st));
+  MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys, d->p0, d->P_local, base, rank, at<uint8_t>(ws, L.xq),
+                       at<uint8_t>(ws, L.xs), rop, por, st));
+  MOE_TRY(launch_gemm1_a16(x, d->T, offsets, por, d->k, pw1, pw1s, act, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_gemm2_a16(act, d->T_max * d->k, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st));
+  MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, st));
+  return MOE_OK;
+}
+
 }  // extern "C"

@@ -101,4 +101,15 @@ size_t router_partial_bytes(int T_max, int E, int H);
 hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, float* partial, int T, int E, int H,
                          hipStream_t st);
 
+// a16w4 variant (kernels_a16.hip): bf16 rows on MXFP4 experts, weights
+// expanded to bf16 in registers, bf16 MFMA.  GEMM1 reads the bf16 input row of
+// each bucketed row's token (pair_of_row / k) and writes bf16 act rows
+// [rows, F]; GEMM2 reads those and writes f32 y rows [rows, H].  Byte sizes of
+// the inputs (T H 2 and rows_max F 2) must stay below 2^31.
+hipError_t launch_gemm1_a16(const uint16_t* x, int T, const int32_t* offsets, const int32_t* pair_of_row, int k,
+                            const uint8_t* pw1, const uint8_t* pw1s, uint16_t* act, int H, int F, int P_local,
+                            hipStream_t st);
+hipError_t launch_gemm2_a16(const uint16_t* act, int rows_max, const int32_t* offsets, const uint8_t* pw2,
+                            const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
+
 }  // namespace moe

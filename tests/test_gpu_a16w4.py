@@ -1,0 +1,192 @@
+"""GPU parity of the a16w4 variant (moe_forward_a16w4: bf16 activations on the
+MXFP4 experts) against the oracle.
+
+Bit-exact: routing, remap, histogram, buckets and row maps.  The bf16 act
+rows: every GPU value must be the bf16 rounding of some value within the f32
+accumulation bound of the float64 act (2^-14 of the sum of absolute products,
+the ratio the a8w4 checks use).  Output: normwise <= 1e-2 and elementwise
+<= 5e-2 where |ref| > 1e-3 against the oracle's GEMM2 + combine applied to the
+GPU's own act rows ("conditioned"), and normwise <= 1e-2 end to end.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_layer_sigmoid_amd as mx
+import synth
+from oracle import a16w4 as oa
+from oracle import formats as fm
+from oracle import moe as om
+from tests import parity as P
+from tests.test_gpu_parity import _say
+
+pytestmark = pytest.mark.gpu
+
+ACC_REL = 2.0 ** -14
+
+
+def _run(wl, buf=None):
+    d = mx.Dims.of(wl.dims)
+    buf = buf or P.upload(wl)
+    out = torch.full((max(d.T, 1), d.H), -1, dtype=torch.int16, device="cuda")
+    hist = torch.zeros(d.P_total, dtype=torch.int32, device="cuda")
+    TK, TMK = d.T * d.k, d.T_max * d.k
+    taps = dict(topk_ids=torch.zeros(max(TK, 1), dtype=torch.int32, device="cuda"),
+                topk_w=torch.zeros(max(TK, 1), dtype=torch.float32, device="cuda"),
+                phys_ids=torch.zeros(max(TK, 1), dtype=torch.int32, device="cuda"),
+                counts=torch.zeros(d.P_local, dtype=torch.int32, device="cuda"),
+                offsets=torch.zeros(d.P_local + 1, dtype=torch.int32, device="cuda"),
+                row_of_pair=torch.zeros(max(TK, 1), dtype=torch.int32, device="cuda"),
+                pair_of_row=torch.zeros(max(TMK, 1), dtype=torch.int32, device="cuda"))
+    act = torch.zeros((max(TMK, 1), d.F), dtype=torch.int16, device="cuda")
+    mx.moe_forward_a16w4(d, buf["x"], buf["logits"], buf["w1"], buf["w1s"], buf["w2"], buf["w2s"], buf["rep_count"],
+                         buf["rep_slots"], out, mx.a16w4_workspace(d), load_hist=hist, taps=taps, act=act)
+    torch.cuda.synchronize()
+    c = {n: v.cpu().numpy() for n, v in taps.items()}
+    rows = int(c["offsets"][d.P_local]) if d.T else 0
+    return dict(out=out.cpu().numpy().view(np.uint16)[:d.T], hist=hist.cpu().numpy(),
+                topk_ids=c["topk_ids"][:TK].reshape(d.T, d.k), topk_w=c["topk_w"][:TK].reshape(d.T, d.k),
+                phys_ids=c["phys_ids"][:TK].reshape(d.T, d.k), counts=c["counts"], offsets=c["offsets"],
+                row_of_pair=c["row_of_pair"][:TK], pair_of_row=c["pair_of_row"][:rows],
+                act=act.cpu().numpy().view(np.uint16)[:rows])
+
+
+def _front(res, ref, d):
+    assert np.array_equal(res["topk_ids"], ref["topk_ids"])
+    assert np.all(np.abs(res["topk_w"] - ref["topk_w"]) <= P.W_RTOL * np.abs(ref["topk_w"]))
+    assert np.array_equal(res["phys_ids"], ref["phys_ids"])
+    assert np.array_equal(res["hist"], ref["load_hist"])
+    assert np.array_equal(res["counts"], ref["counts"])
+    assert np.array_equal(res["offsets"], ref["offsets"])
+    assert np.array_equal(res["row_of_pair"], ref["row_of_pair"])
+    assert np.array_equal(res["pair_of_row"], ref["pair_of_row"])
+
+
+def _bf16_ulp(v):
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def _check_slots(wl, res, slots):
+    """act rows of the listed slots within the bound; returns the conditioned
+    y rows {row: y} computed from the GPU's act."""
+    d = wl.dims
+    x = fm.bf16_to_f64(wl.x)
+    off, por = res["offsets"], res["pair_of_row"]
+    y_c, worst = {}, 0.0
+    for s in slots:
+        lo, hi = int(off[s]), int(off[s + 1])
+        if hi == lo:
+            continue
+        xr = x[por[lo:hi] // d.k]
+        r = oa.expert_rows(xr, wl.w1[s], wl.w1s[s], wl.w2[s], wl.w2s[s], d.F)
+        eps = oa.act_error_bound(xr, wl.w1[s], wl.w1s[s], r["h"], d.F, ACC_REL)
+        got = fm.bf16_to_f64(res["act"][lo:hi])
+        tol = eps + 0.5 * _bf16_ulp(np.maximum(np.abs(got), np.abs(r["act"]))) + 1e-30
+        err = np.abs(got - r["act"])
+        assert np.all(err <= tol), f"slot {s}: act off by {float((err / tol).max()):.3g} of the bound"
+        worst = max(worst, float((err / tol).max()))
+        y = om.gemm2(got, wl.w2[s], wl.w2s[s])
+        for i in range(hi - lo):
+            y_c[lo + i] = y[i]
+    return y_c, worst
+
+
+def _conditioned(tokens, res, y_c, d):
+    """The oracle's combine (float64 routing weights, ascending j) of the
+    conditioned y rows for the listed tokens."""
+    rop = res["row_of_pair"].reshape(d.T, d.k)
+    out = np.zeros((len(tokens), d.H))
+    for n, t in enumerate(tokens):
+        for j in range(d.k):
+            r = int(rop[t, j])
+            if r >= 0:
+                out[n] += float(res["w_ref"][t, j]) * y_c[r]
+    return out
+
+
+def _full(wl):
+    d = wl.dims
+    _say(f"[case] a16w4 {wl.name} T={d.T} H={d.H} F={d.F} E={d.E} k={d.k} P={d.P_total}/{d.p0}+{d.P_local}")
+    res = _run(wl)
+    ref = oa.forward(wl)
+    _front(res, ref, d)
+    res["w_ref"] = ref["topk_w"]
+    y_c, worst = _check_slots(wl, res, range(d.P_local))
+    toks = list(range(d.T))
+    cond = _conditioned(toks, res, y_c, d)
+    n1 = P.check_out(res["out"], cond, "conditioned")
+    n2, _ = P.rel_errors(fm.bf16_to_f64(res["out"]), ref["out"])
+    assert n2 <= P.OUT_NORM_TOL, n2
+    none_local = (ref["row_of_pair"].reshape(d.T, d.k) < 0).all(1)
+    assert np.all(res["out"][none_local] == 0)
+    _say(f"   ok: act within {worst:.2f} of its bound, out cond {n1}, uncond {n2:.2e}")
+    return res
+
+
+def test_a16w4_tiny():
+    _full(synth.make("tiny"))
+
+
+def test_a16w4_ragged_remote_and_padded_k():
+    # 200 tokens, H = F = 384 (K padded to 1024 in the packed weights), half
+    # the slots on another rank, replicas over two ranks
+    _full(synth.make_custom(T=200, H=384, F=384, E=16, k=4, P_local=10, p0=10, redundant=4, ranks=2, seed=77,
+                            token_id_base=999))
+
+
+def test_a16w4_many_rows_per_slot():
+    # ~100 rows per slot: several 16-row passes per block
+    _full(synth.make_custom(T=400, H=256, F=256, E=8, k=2, P_local=8, seed=78))
+
+
+def test_a16w4_single_token_and_all_remote():
+    _full(synth.make_custom(T=1, H=256, F=128, E=8, k=2, P_local=8, seed=79, T_max=64))
+    wl = synth.make("tiny")
+    wl.rep_slots = wl.rep_slots + 100
+    wl.dims = wl.dims.replace(P_total=200)
+    res = _run(wl)
+    assert np.all(res["out"] == 0) and res["hist"].sum() == wl.dims.T * wl.dims.k
+
+
+def test_a16w4_decode_share_512_tokens():
+    """The decode share's shapes (d_model 7168, d_ff 2048, 384 experts, top-6,
+    48 local): integer stages in full, act and output on sampled slots and
+    tokens."""
+    wl = synth.make("decode512")
+    d = wl.dims
+    _say(f"[case] a16w4 decode share T={d.T}")
+    res = _run(wl)
+    ids, w = om.route(wl.logits, d.k)
+    phys, hist = om.remap_record(ids, wl.rep_count, wl.rep_slots, d.token_id_base, d.P_total)
+    counts, offsets, rop, por = om.buckets(phys, d.p0, d.P_local)
+    _front(res, dict(topk_ids=ids, topk_w=w, phys_ids=phys, load_hist=hist, counts=counts, offsets=offsets,
+                     row_of_pair=rop, pair_of_row=por), d)
+    res["w_ref"] = w
+    rng = np.random.default_rng(5)
+    toks = np.sort(rng.choice(d.T, size=16, replace=False))
+    slots = set(rng.choice(d.P_local, size=2, replace=False).tolist())
+    r2 = rop.reshape(d.T, d.k)
+    for t in toks:
+        for j in range(d.k):
+            if r2[t, j] >= 0:
+                slots.add(int(phys[t, j]) - d.p0)
+    y_c, worst = _check_slots(wl, res, sorted(slots))
+    cond = _conditioned(list(toks), res, y_c, d)
+    n1 = P.check_out(res["out"][toks], cond, "conditioned")
+    unc = np.stack([oa.forward_token(wl, int(t)) for t in toks[:6]])
+    n2, _ = P.rel_errors(fm.bf16_to_f64(res["out"][toks[:6]]), unc)
+    assert n2 <= P.OUT_NORM_TOL
+    _say(f"   ok: {len(slots)} slots, act within {worst:.2f} of its bound, out cond {n1}, uncond {n2:.2e}")
+
+
+def test_a16w4_zero_tokens():
+    wl = synth.make_custom(T=0, H=256, F=128, E=8, k=2, P_local=8, seed=80, T_max=16)
+    d = mx.Dims.of(wl.dims)
+    buf = P.upload(synth.make_custom(T=16, H=256, F=128, E=8, k=2, P_local=8, seed=80))
+    out = torch.full((1, d.H), 7, dtype=torch.int16, device="cuda")
+    mx.moe_forward_a16w4(d, buf["x"], buf["logits"], buf["w1"], buf["w1s"], buf["w2"], buf["w2s"], buf["rep_count"],
+                         buf["rep_slots"], out, mx.a16w4_workspace(d))
+    torch.cuda.synchronize()
+    assert torch.all(out == 7)
