@@ -4,7 +4,8 @@
 // bf16 activations].  gfx950's block-scaled MFMA takes fp8/fp6/fp4 operands
 // only, so each weight block is expanded to bf16 in registers (exactly: an
 // e2m1 value times its e8m0 scale is a bf16 with at most two significant
-// bits) and multiplied on the bf16 16x16x32 MFMA.
+// bits; byte-table lookups, about 2.5 integer instructions per value) and
+// multiplied on the bf16 16x16x32 MFMA.
 //
 // One block of 4 waves per (local slot, 64 output columns); wave w owns 16
 // columns: for GEMM1 the gate tile and the matching up tile (SwiGLU pairs
@@ -30,31 +31,47 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kA16Cols = 64;  // output columns per block (16 per wave)
 
-// Two e2m1 codes -> two bf16 of one dword: x holds code n0 in bits 0-3 and n1
-// in bits 16-19, c16 = (scale - 1) << 7.  With v = n & 7 the magnitude is
-// v >= 2: (1 + (v & 1) / 2) 2^(v/2 - 1), v = 1: 1/2, v = 0: 0, so the bf16 bits
-// are 64 v + c16 (v >= 2), c16 (v = 1), 0 (v = 0), the sign bit from bit 3.
-// Each step stays inside its 16-bit half (no carry crosses: the largest half
-// is 448 + 254 * 128 < 2^16).  Exact for scale bytes 2 ... 252, where every
-// value is a normal bf16.
-__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t x, uint32_t c16) {
-  const uint32_t v = x & 0x00070007u;
-  const uint32_t h = (v >> 1) & 0x00030003u;
-  const uint32_t ge2 = ((h + 0x7FFF7FFFu) >> 15) & 0x00010001u;  // per half: v >= 2
-  const uint32_t ge1 = ((v + 0x7FFF7FFFu) >> 15) & 0x00010001u;  // per half: v >= 1
-  const uint32_t mag = ((v & __umul24(ge2, 0xFFFFu)) << 6) + __umul24(ge1, c16);
-  return mag | ((x & 0x00080008u) << 12);
+// bf16 bits of the eight e2m1 magnitudes v = 0 ... 7 under scale byte sb, as
+// byte tables for v_perm: low bytes in l0 (v = 0..3) and l1 (v = 4..7), high
+// bytes in h0 / h1.  The value is 2^(sb-127) times {0, 1/2, 1, 3/2, 2, 3, 4, 6},
+// i.e. bits 0 (v = 0) and c + 64 v' with c = (sb - 1) << 7, v' = 0 for v = 1
+// and v for v >= 2: the low byte depends only on the parity of sb - 1 and the
+// high byte is (sb - 1) / 2 plus a carry of 0, 1 or 2.  Exact for scale bytes
+// 2 ... 252, where every value is a normal bf16 (the high byte stays below 128).
+struct Bf16Tab {
+  uint32_t l0, l1, h0, h1;
+};
+
+__device__ __forceinline__ Bf16Tab bf16_tables(uint32_t sb) {
+  const uint32_t odd = (sb - 1u) & 1u, hb = ((sb - 1u) >> 1) & 0x7Fu;
+  Bf16Tab t;
+  t.l0 = odd ? 0x40008000u : 0xC0800000u;
+  t.l1 = odd ? 0x4000C080u : 0xC0804000u;
+  t.h0 = hb * 0x01010100u + (odd ? 0x01010000u : 0u);
+  t.h1 = hb * 0x01010101u + (odd ? 0x02020101u : 0x01010101u);
+  return t;
 }
 
-// Elements [8 m, 8 m + 8) of a lane's 32-element block (dword m of its 16
-// bytes, element 2 q in the low nibble of byte q) as a bf16 operand.
-__device__ __forceinline__ v4i dequant8(uint32_t a, uint32_t c16) {
+// Elements [8 m, 8 m + 8) of a lane's 32-element block (dword `a` = dword m
+// of its 16 bytes, element 2 q in the low nibble of byte q) as a bf16 operand:
+// byte-table lookups of the magnitudes (v_perm selectors 0-3 pick the second
+// source, 4-7 the first), the sign bits or-ed into the high bytes, then the
+// low / high bytes interleaved into four dwords of two bf16 each.
+__device__ __forceinline__ v4i expand8(uint32_t a, const Bf16Tab& t) {
+  const uint32_t ve = a & 0x07070707u, vo = (a >> 4) & 0x07070707u;  // even / odd elements
+  const uint32_t le = __builtin_amdgcn_perm(t.l1, t.l0, ve);
+  const uint32_t he = __builtin_amdgcn_perm(t.h1, t.h0, ve) | ((a << 4) & 0x80808080u);
+  const uint32_t lo = __builtin_amdgcn_perm(t.l1, t.l0, vo);
+  const uint32_t ho = __builtin_amdgcn_perm(t.h1, t.h0, vo) | (a & 0x80808080u);
+  const uint32_t e02 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // elements 0, 2
+  const uint32_t e46 = __builtin_amdgcn_perm(he, le, 0x07030602u);  // elements 4, 6
+  const uint32_t o13 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // elements 1, 3
+  const uint32_t o57 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // elements 5, 7
   v4i r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t x = ((a >> (8 * q)) & 0xFu) | (((a >> (8 * q + 4)) & 0xFu) << 16);
-    r[q] = (int)e2m1x2_to_bf16x2(x, c16);
-  }
+  r[0] = (int)__builtin_amdgcn_perm(o13, e02, 0x05040100u);
+  r[1] = (int)__builtin_amdgcn_perm(o13, e02, 0x07060302u);
+  r[2] = (int)__builtin_amdgcn_perm(o57, e46, 0x05040100u);
+  r[3] = (int)__builtin_amdgcn_perm(o57, e46, 0x07060302u);
   return r;
 }
 
@@ -124,9 +141,9 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
           const uint32_t sb = ((uint32_t)(bi < 4 ? sc[j].x : sc[j].y) >> (8 * (bi & 3))) & 0xFFu;
-          const uint32_t c16 = ((sb - 1u) & 0xFFu) << 7;
+          const Bf16Tab tab = bf16_tables(sb);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[j] = mfma_bf16(dequant8((uint32_t)a[j][m], c16), b[m], acc[j]);
+          for (int m = 0; m < 4; ++m) acc[j] = mfma_bf16(expand8((uint32_t)a[j][m], tab), b[m], acc[j]);
         }
       }
     }
