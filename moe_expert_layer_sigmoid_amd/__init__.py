@@ -108,11 +108,9 @@ def lib() -> ctypes.CDLL:
         L.moe_router_logits.restype = I
         L.moe_eplb_rebalance.argtypes = [I, I, I, I, P, P, P, P, P]
         L.moe_eplb_migrate.argtypes = [D, P, I, P, P, P, P, P, P, P, P, P]
-        for n in ("moe_eplb_rebalance", "moe_eplb_migrate", "moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute", "moe_grouped_gemm1_swiglu",
-                  "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
-                  "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
-           "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m",
-           "moe_a16w4_workspace_bytes", "moe_forward_a16w4"):
+        for n in ("moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute",
+                  "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs",
+                  "moe_grouped_gemm2_combine_pairs", "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate"):
             getattr(L, n).restype = I
         _lib_handle = L
     return _lib_handle

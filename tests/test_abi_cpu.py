@@ -122,3 +122,52 @@ def test_zero_tokens_is_a_no_op():
     P = ctypes.c_void_p
     assert L.moe_route(ctypes.byref(d), P(0x1000), P(0x2000), P(0x3000), None) == 0
     assert L.moe_route(ctypes.byref(d), None, P(0x2000), P(0x3000), None) == -1
+
+
+def test_next_row_entry_points_validate_on_the_host():
+    """Router projection, graph-bucket forward, a16w4 forward and EPLB
+    migration: argument errors come back before any launch; zero tokens
+    launch nothing."""
+    L = mx.lib()
+    P = ctypes.c_void_p
+    d = _dims()
+    G = [P(a) for a in GOOD]
+    # router projection
+    rb = mx.moe_router_workspace_bytes(d)
+    assert rb > 0 and mx.moe_router_workspace_bytes(_dims(T_max=8192)) > rb
+    assert L.moe_router_logits(ctypes.byref(d), G[0], G[1], G[2], G[3], rb - 1, None) == -3
+    assert L.moe_router_logits(ctypes.byref(d), None, G[1], G[2], G[3], rb, None) == -1
+    assert L.moe_router_logits(ctypes.byref(d), G[0], G[1], P(0x2004), G[3], rb, None) == -1
+    z = _dims(T=0)
+    assert L.moe_router_logits(ctypes.byref(z), G[0], G[1], G[2], G[3], mx.moe_router_workspace_bytes(z), None) == 0
+
+    # graph-bucket small-input forward
+    need = mx.moe_workspace_bytes(d)
+    args = G[:10]
+    assert L.moe_forward_small_m(ctypes.byref(d), None, *args, None, P(0x100000), need, None) == -1
+    assert L.moe_forward_small_m(ctypes.byref(d), P(0x1002), *args, None, P(0x100000), need, None) == -1
+    big = _dims(T=1025, T_max=1025)
+    assert L.moe_forward_small_m(ctypes.byref(big), P(0x1000), *args, None, P(0x100000),
+                                 mx.moe_workspace_bytes(big), None) == -2
+    assert L.moe_forward_small_m(ctypes.byref(z), P(0x1000), *args, None, P(0x100000),
+                                 mx.moe_workspace_bytes(z), None) == 0
+
+    # a16w4 forward
+    ab = mx.moe_a16w4_workspace_bytes(d)
+    assert ab > need
+    assert L.moe_forward_a16w4(ctypes.byref(d), *args, None, None, P(0x100000), ab - 1, None) == -3
+    bad = list(args)
+    bad[2] = None
+    assert L.moe_forward_a16w4(ctypes.byref(d), *bad, None, None, P(0x100000), ab, None) == -1
+    huge = _dims(T=1, T_max=1 << 20, H=16384)
+    # size queries are size_t through the binding (no 32-bit truncation)
+    assert mx.moe_a16w4_workspace_bytes(huge) > 2 ** 32 and mx.moe_workspace_bytes(huge) > 2 ** 32
+    assert L.moe_forward_a16w4(ctypes.byref(huge), *args, None, None, P(0x100000),
+                               mx.moe_a16w4_workspace_bytes(huge), None) == -2
+    assert L.moe_forward_a16w4(ctypes.byref(z), *args, None, None, P(0x100000),
+                               mx.moe_a16w4_workspace_bytes(z), None) == 0
+
+    # EPLB migration (a valid call would launch: only errors here)
+    assert L.moe_eplb_migrate(ctypes.byref(d), G[0], 0, *G[1:9], None) == -1
+    assert L.moe_eplb_migrate(ctypes.byref(d), G[0], 384, P(0x1001), *G[2:9], None) == -1
+    assert L.moe_eplb_migrate(ctypes.byref(_dims(H=100)), G[0], 384, *G[1:9], None) == -1
