@@ -303,6 +303,16 @@ def test_sweep_16384_tokens():
     assert res["chosen"] == "large_m"
 
 
+def test_prefill_ep8_rank_share_65536_tokens():
+    """The EP-shaped prefill share the benchmark times (8 ranks x 8192 tokens
+    routed into this GPU's 48 experts, ~1030 rows per slot: nine 128-token
+    blocks per slot on the tiled kernels), compared like the other full-size
+    workloads."""
+    wl = synth.make_ep_shaped(8)
+    res = _big_check(wl, n_slots=2, n_tokens=12, path="large_m")
+    assert res["chosen"] == "large_m" and res["rows"] > 45000
+
+
 def test_skewed_routing_with_eplb_8192_tokens():
     wl = synth.make("eplb8192")
     res = _big_check(wl)
