@@ -36,30 +36,39 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
                                                  0);
 }
 
-constexpr int kRouterBM = 128;          // experts per block
-constexpr int kRouterBK = 128;          // K columns per stage
-constexpr int kRouterRow = 272;         // LDS bytes per staged row (256 + 16 pad)
 constexpr int kRouterDepth = 3;         // stages of global loads in flight
 
-template <int NB>
+// Staged rows: BK bf16 columns (2 BK bytes) plus 16 bytes of padding, so that
+// the 16 rows of a 16-lane ds_read_b128 phase fall on distinct banks (row
+// strides of 68 and 36 dwords map 16 rows onto 16 distinct 4-bank groups).
+template <int BK>
+constexpr int router_row() {
+  return 2 * BK + 16;
+}
+
+template <int NB, int BM, int BK>
 struct RouterSmem {
-  uint8_t a[2][kRouterBM * kRouterRow];
-  uint8_t b[2][16 * NB * kRouterRow];
+  uint8_t a[2][BM * router_row<BK>()];
+  uint8_t b[2][16 * NB * router_row<BK>()];
 };
 
-template <int NB>
+// NB: token tiles of 16 per block; BM: experts per block; BK: K columns per stage.
+template <int NB, int BM, int BK>
 __global__ void __launch_bounds__(64 * kRouterWaves)
     k_router_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, float* __restrict__ out, int T,
                   int E, int H, int klen, int gx, int gy, int tiles) {
+  constexpr int kRouterBM = BM, kRouterBK = BK, kRouterRow = router_row<BK>();
+  constexpr int PR = BK / 8;                                    // 16-byte pieces per staged row
   constexpr int BN = 16 * NB;                                   // tokens per block
   constexpr int NT = 64 * kRouterWaves;                         // threads
   constexpr int WN = NB >= 2 ? 2 : 1;                           // waves along tokens
   constexpr int WM = kRouterWaves / WN;                         // waves along experts
   constexpr int TI = kRouterBM / (16 * WM);                     // expert tiles per wave
   constexpr int TJ = NB / WN;                                   // token tiles per wave
-  constexpr int PA = kRouterBM * 16 / NT;                       // 16-byte pieces per thread: A
-  constexpr int PB = (BN * 16 + NT - 1) / NT;                   // and B (the last may be partial)
-  __shared__ __align__(16) RouterSmem<NB> sm;
+  constexpr int PA = kRouterBM * PR / NT;                       // 16-byte pieces per thread: A
+  constexpr int PB = (BN * PR + NT - 1) / NT;                   // and B (the last may be partial)
+  static_assert(TI * 16 * WM == BM && PA * NT == BM * PR && NT % PR == 0, "router tile shape");
+  __shared__ __align__(16) RouterSmem<NB, BM, BK> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -75,18 +84,18 @@ __global__ void __launch_bounds__(64 * kRouterWaves)
   const int e0 = bx * kRouterBM, t0 = by * BN, kb = bz * klen;
   const int stages = (min(H, kb + klen) - kb) / kRouterBK;  // H, klen: multiples of 128
 
-  // this thread's pieces: piece index i = tid + NT q -> row i / 16, bytes 16 (i % 16)
-  const int pcol = tid & 15;
+  // this thread's pieces: piece index i = tid + NT q -> row i / PR, bytes 16 (i % PR)
+  const int pcol = tid % PR;
   const v4i* ga[PA];
   const v4i* gb[PB];
 #pragma unroll
   for (int q = 0; q < PA; ++q) {
-    const int row = min(e0 + (tid + NT * q) / 16, E - 1);  // rows past E: a valid row, results not stored
+    const int row = min(e0 + (tid + NT * q) / PR, E - 1);  // rows past E: a valid row, results not stored
     ga[q] = reinterpret_cast<const v4i*>(wg + (size_t)row * H + kb) + pcol;
   }
 #pragma unroll
   for (int q = 0; q < PB; ++q) {
-    const int row = min(t0 + min((tid + NT * q) / 16, BN - 1), T - 1);
+    const int row = min(t0 + min((tid + NT * q) / PR, BN - 1), T - 1);
     gb[q] = reinterpret_cast<const v4i*>(x + (size_t)row * H + kb) + pcol;
   }
   // kRouterDepth register sets of staged pieces: the global loads of stage
@@ -104,11 +113,11 @@ __global__ void __launch_bounds__(64 * kRouterWaves)
   auto stash = [&](int set, int buf) {
 #pragma unroll
     for (int q = 0; q < PA; ++q)
-      *reinterpret_cast<v4i*>(sm.a[buf] + ((tid + NT * q) / 16) * kRouterRow + pcol * 16) = ra[set][q];
+      *reinterpret_cast<v4i*>(sm.a[buf] + ((tid + NT * q) / PR) * kRouterRow + pcol * 16) = ra[set][q];
 #pragma unroll
     for (int q = 0; q < PB; ++q)
-      if (tid + NT * q < BN * 16)
-        *reinterpret_cast<v4i*>(sm.b[buf] + ((tid + NT * q) / 16) * kRouterRow + pcol * 16) = rb[set][q];
+      if (tid + NT * q < BN * PR)
+        *reinterpret_cast<v4i*>(sm.b[buf] + ((tid + NT * q) / PR) * kRouterRow + pcol * 16) = rb[set][q];
   };
 
   v4f acc[TI][TJ];
@@ -202,8 +211,9 @@ __global__ void __launch_bounds__(256) k_router_reduce(const float* __restrict__
 
 RouterPlan router_plan(int T, int E, int H) {
   RouterPlan p;
-  p.ni = T >= kRouterLargeT ? 8 : (T >= kRouterMidT ? 4 : 1);  // token tiles per block (NB)
-  p.gx = (E + kRouterBM - 1) / kRouterBM;
+  p.ni = T >= kRouterHugeT ? 16 : (T >= kRouterLargeT ? 8 : (T >= kRouterMidT ? 4 : 1));  // token tiles per block
+  p.bm = p.ni == 16 ? kRouterWideBM : 128;
+  p.gx = (E + p.bm - 1) / p.bm;
   p.gy = (T + 16 * p.ni - 1) / (16 * p.ni);
   const int blocks = p.gx * p.gy;
   int S = blocks >= kRouterMinBlocks ? 1 : (kRouterMinBlocks + blocks - 1) / blocks;
@@ -216,11 +226,14 @@ RouterPlan router_plan(int T, int E, int H) {
 }
 
 size_t router_partial_bytes(int T_max, int E, int H) {
-  // splits <= ceil(kRouterMinBlocks / blocks) and blocks >= gx * T / (16 NB), NB <= 8,
-  // so splits * T <= kRouterMinBlocks * 128 / gx + T for every T <= T_max
+  // splits <= ceil(kRouterMinBlocks / blocks) and blocks >= gx * T / (16 ni), so
+  // splits * T <= kRouterMinBlocks * 16 ni / gx + T for every T <= T_max; the
+  // larger bound of the two tile heights (ni <= 8 with 128 experts, ni = 16 with
+  // the wide tiles)
   (void)H;
-  const int gx = (E + kRouterBM - 1) / kRouterBM;
-  const size_t tok = (size_t)kRouterMinBlocks * 16 * 8 / gx + 1 + (size_t)T_max;
+  const size_t g128 = (size_t)(E + 127) / 128, gw = (size_t)(E + kRouterWideBM - 1) / kRouterWideBM;
+  const size_t a = (size_t)kRouterMinBlocks * 16 * 8 / g128, b = (size_t)kRouterMinBlocks * 16 * 16 / gw;
+  const size_t tok = (a > b ? a : b) + 1 + (size_t)T_max;
   return tok * E * sizeof(float);
 }
 
@@ -230,12 +243,18 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, f
   float* dst = p.splits > 1 ? partial : logits;
   const int tiles = p.gx * p.gy * p.splits;
   dim3 grid((tiles + kXcds - 1) / kXcds * kXcds), block(64 * kRouterWaves);
-  if (p.ni == 8)
-    hipLaunchKernelGGL(k_router_gemm<8>, grid, block, 0, st, x, wg, dst, T, E, H, p.klen, p.gx, p.gy, tiles);
+  if (p.ni == 16)
+    hipLaunchKernelGGL((k_router_gemm<16, kRouterWideBM, 64>), grid, block, 0, st, x, wg, dst, T, E, H, p.klen, p.gx,
+                       p.gy, tiles);
+  else if (p.ni == 8)
+    hipLaunchKernelGGL((k_router_gemm<8, 128, 128>), grid, block, 0, st, x, wg, dst, T, E, H, p.klen, p.gx, p.gy,
+                       tiles);
   else if (p.ni == 4)
-    hipLaunchKernelGGL(k_router_gemm<4>, grid, block, 0, st, x, wg, dst, T, E, H, p.klen, p.gx, p.gy, tiles);
+    hipLaunchKernelGGL((k_router_gemm<4, 128, 128>), grid, block, 0, st, x, wg, dst, T, E, H, p.klen, p.gx, p.gy,
+                       tiles);
   else
-    hipLaunchKernelGGL(k_router_gemm<1>, grid, block, 0, st, x, wg, dst, T, E, H, p.klen, p.gx, p.gy, tiles);
+    hipLaunchKernelGGL((k_router_gemm<1, 128, 128>), grid, block, 0, st, x, wg, dst, T, E, H, p.klen, p.gx, p.gy,
+                       tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t n = (size_t)T * E;

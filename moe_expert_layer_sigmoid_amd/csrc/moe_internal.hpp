@@ -91,12 +91,17 @@ hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_
 // (Measured at 384 experts, d_model 7168: 512 tokens in 64-token tiles take
 // 17.5 us, in 16-token tiles 26.7 us -- each token tile reads the whole gate
 // -- and in 128-token tiles 21.9 us; 512 blocks and 32 splits 23.3 us.)
+// From kRouterHugeT tokens the tiles are kRouterWideBM experts x 256 tokens in
+// 64-column stages (the gate is re-read once per 256 tokens, x once per 192
+// experts).
+constexpr int kRouterHugeT = 4096;
+constexpr int kRouterWideBM = 192;
 constexpr int kRouterLargeT = 4096;
 constexpr int kRouterMidT = 256;
 constexpr int kRouterMinBlocks = 256;
 constexpr int kRouterMaxSplits = 16;
 struct RouterPlan {
-  int ni, gx, gy, splits, klen;
+  int ni, bm, gx, gy, splits, klen;
 };
 RouterPlan router_plan(int T, int E, int H);
 // Bytes of `partial` any T <= T_max needs (an upper bound).

@@ -48,7 +48,7 @@ def _check_logits(x, wg, got, H):
 
 
 @pytest.mark.parametrize("T,H,E", [(64, 256, 8), (1, 256, 8), (200, 384, 13), (37, 128, 1024),
-                                   (3000, 640, 96), (2048, 7168, 384)])
+                                   (3000, 640, 96), (2048, 7168, 384), (5000, 384, 200)])
 def test_router_logits_small_and_ragged(T, H, E):
     _say(f"[case] router T={T} H={H} E={E}")
     x, wg, got = _run(T, H, E)
