@@ -4,12 +4,12 @@
 // bf16 activations].  gfx950's block-scaled MFMA takes fp8/fp6/fp4 operands
 // only, so each weight block is expanded to bf16 in registers (exactly: an
 // e2m1 value times its e8m0 scale is a bf16 with at most two significant
-// bits; byte-table lookups, about 2.5 integer instructions per value) and
-// multiplied on the bf16 16x16x32 MFMA.
+// bits; the hardware conversion, two values per instruction) and multiplied
+// on the bf16 16x16x32 MFMA.
 //
-// One block of 4 waves per (local slot, 64 output columns); wave w owns 16
-// columns: for GEMM1 the gate tile and the matching up tile (SwiGLU pairs
-// registers of the same lane), for GEMM2 one tile of H.  The packed weight
+// One block of 4 waves per (local slot, 128 columns of F | 256 rows of H);
+// wave w owns four weight tiles: for GEMM1 two gate tiles and the matching up
+// tiles (SwiGLU pairs registers of the same lane), for GEMM2 64 rows of H.  The packed weight
 // layout of the a8w4 kernels is read as is: lane 16 g + r of half-step i of K
 // step st holds row r's 32-block b = 8 st + 4 i + g, and MFMA m of that
 // half-step takes elements [8 m, 8 m + 8) of every lane's block -- the K order
@@ -29,49 +29,27 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int kA16Cols = 64;  // output columns per block (16 per wave)
-
-// bf16 bits of the eight e2m1 magnitudes v = 0 ... 7 under scale byte sb, as
-// byte tables for v_perm: low bytes in l0 (v = 0..3) and l1 (v = 4..7), high
-// bytes in h0 / h1.  The value is 2^(sb-127) times {0, 1/2, 1, 3/2, 2, 3, 4, 6},
-// i.e. bits 0 (v = 0) and c + 64 v' with c = (sb - 1) << 7, v' = 0 for v = 1
-// and v for v >= 2: the low byte depends only on the parity of sb - 1 and the
-// high byte is (sb - 1) / 2 plus a carry of 0, 1 or 2.  Exact for scale bytes
-// 2 ... 252, where every value is a normal bf16 (the high byte stays below 128).
-struct Bf16Tab {
-  uint32_t l0, l1, h0, h1;
-};
-
-__device__ __forceinline__ Bf16Tab bf16_tables(uint32_t sb) {
-  const uint32_t odd = (sb - 1u) & 1u, hb = ((sb - 1u) >> 1) & 0x7Fu;
-  Bf16Tab t;
-  t.l0 = odd ? 0x40008000u : 0xC0800000u;
-  t.l1 = odd ? 0x4000C080u : 0xC0804000u;
-  t.h0 = hb * 0x01010100u + (odd ? 0x01010000u : 0u);
-  t.h1 = hb * 0x01010101u + (odd ? 0x02020101u : 0x01010101u);
-  return t;
+// Output columns per block: GEMM1 32 per wave (two gate and two up tiles),
+// GEMM2 64 per wave (four tiles of H).
+template <bool G1>
+constexpr int a16_cols() {
+  return G1 ? 128 : 256;
 }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
 // Elements [8 m, 8 m + 8) of a lane's 32-element block (dword `a` = dword m
-// of its 16 bytes, element 2 q in the low nibble of byte q) as a bf16 operand:
-// byte-table lookups of the magnitudes (v_perm selectors 0-3 pick the second
-// source, 4-7 the first), the sign bits or-ed into the high bytes, then the
-// low / high bytes interleaved into four dwords of two bf16 each.
-__device__ __forceinline__ v4i expand8(uint32_t a, const Bf16Tab& t) {
-  const uint32_t ve = a & 0x07070707u, vo = (a >> 4) & 0x07070707u;  // even / odd elements
-  const uint32_t le = __builtin_amdgcn_perm(t.l1, t.l0, ve);
-  const uint32_t he = __builtin_amdgcn_perm(t.h1, t.h0, ve) | ((a << 4) & 0x80808080u);
-  const uint32_t lo = __builtin_amdgcn_perm(t.l1, t.l0, vo);
-  const uint32_t ho = __builtin_amdgcn_perm(t.h1, t.h0, vo) | (a & 0x80808080u);
-  const uint32_t e02 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // elements 0, 2
-  const uint32_t e46 = __builtin_amdgcn_perm(he, le, 0x07030602u);  // elements 4, 6
-  const uint32_t o13 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // elements 1, 3
-  const uint32_t o57 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // elements 5, 7
+// of its 16 bytes, element 2 q in the low nibble of byte q) as a bf16
+// operand: gfx950's v_cvt_scalef32_pk_bf16_fp4 turns byte q into the two bf16
+// e2m1(code) * scale, low nibble in the low half.  `scale` = 2^(sb - 127) as
+// an f32; every product is exact for scale bytes 2 ... 252 (an e2m1 value
+// times a power of two has at most two significant bits).
+__device__ __forceinline__ v4i expand8(uint32_t a, float scale) {
   v4i r;
-  r[0] = (int)__builtin_amdgcn_perm(o13, e02, 0x05040100u);
-  r[1] = (int)__builtin_amdgcn_perm(o13, e02, 0x07060302u);
-  r[2] = (int)__builtin_amdgcn_perm(o57, e46, 0x05040100u);
-  r[3] = (int)__builtin_amdgcn_perm(o57, e46, 0x07060302u);
+  r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, scale, 0));
+  r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, scale, 1));
+  r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, scale, 2));
+  r[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, scale, 3));
   return r;
 }
 
@@ -88,23 +66,26 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
                                                  const int32_t* __restrict__ pair_of_row, int k,
                                                  const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws,
                                                  uint16_t* __restrict__ act, float* __restrict__ y, int H, int F) {
-  constexpr int NW = G1 ? 2 : 1;  // weight tiles per wave
+  constexpr int NW = 4;  // weight tiles per wave
+  constexpr int kA16Cols = a16_cols<G1>(), WC = kA16Cols / 4;  // columns per block / wave
   const int K = G1 ? H : F, R = G1 ? 2 * F : H, ncol = G1 ? F : H;
-  const int nfb = ncol / kA16Cols;
+  const int nfb = (ncol + kA16Cols - 1) / kA16Cols;
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nfb, fb = item - s * nfb;
   const int row0 = offsets[s], n = offsets[s + 1] - row0;
   if (n <= 0) return;  // block-uniform: an idle expert reads no weights
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int c0 = fb * kA16Cols + wave * 16;
+  const int c0 = fb * kA16Cols + wave * WC;
+  if (c0 >= ncol) return;  // wave-uniform (the last GEMM2 block when H % 256 == 128); no barriers below
   const PackGeom G = pack_geom((uint32_t)R, (uint32_t)K);
   const int S4 = (int)G.steps;
   const uint8_t* wd[NW];
   const uint8_t* wsc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
-    const int tile = (j == 0 ? c0 : F + c0) / 16;
+    // GEMM1: gate tiles of columns c0, c0 + 16, then the matching up tiles
+    const int tile = G1 ? (j >= 2 ? F : 0) / 16 + (c0 + 16 * (j & 1)) / 16 : (c0 + 16 * j) / 16;
     wd[j] = pw + (size_t)s * G.data_slot + (size_t)tile * G.data_tile + lane * 16;
     wsc[j] = pws + (size_t)s * G.scale_slot + (size_t)tile * G.scale_tile + lane * 8;
   }
@@ -141,9 +122,9 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
           const uint32_t sb = ((uint32_t)(bi < 4 ? sc[j].x : sc[j].y) >> (8 * (bi & 3))) & 0xFFu;
-          const Bf16Tab tab = bf16_tables(sb);
+          const float scale = __uint_as_float(sb << 23);  // 2^(sb - 127); 0 for sb = 0 (zero padding)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[j] = mfma_bf16(expand8((uint32_t)a[j][m], tab), b[m], acc[j]);
+          for (int m = 0; m < 4; ++m) acc[j] = mfma_bf16(expand8((uint32_t)a[j][m], scale), b[m], acc[j]);
         }
       }
     }
@@ -151,16 +132,20 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
     // lane (g, r16) holds rows 4 g + q of each weight tile for token row rr
     const size_t orow = (size_t)(row0 + rr);
     if (G1) {
-      uint32_t p[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float a0 = silu(acc[0][2 * q]) * acc[NW - 1][2 * q];
-        const float a1 = silu(acc[0][2 * q + 1]) * acc[NW - 1][2 * q + 1];
-        p[q] = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
+      for (int u = 0; u < 2; ++u) {  // columns c0 + 16 u + 4 g + [0, 4)
+        uint32_t p[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float a0 = silu(acc[u][2 * q]) * acc[2 + u][2 * q];
+          const float a1 = silu(acc[u][2 * q + 1]) * acc[2 + u][2 * q + 1];
+          p[q] = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
+        }
+        *reinterpret_cast<uint2*>(act + orow * F + c0 + 16 * u + 4 * g) = make_uint2(p[0], p[1]);
       }
-      *reinterpret_cast<uint2*>(act + orow * F + c0 + 4 * g) = make_uint2(p[0], p[1]);
     } else {
-      *reinterpret_cast<v4f*>(y + orow * H + c0 + 4 * g) = acc[0];
+#pragma unroll
+      for (int j = 0; j < NW; ++j) *reinterpret_cast<v4f*>(y + orow * H + c0 + 16 * j + 4 * g) = acc[j];
     }
   }
 }
@@ -170,7 +155,7 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
 hipError_t launch_gemm1_a16(const uint16_t* x, int T, const int32_t* offsets, const int32_t* pair_of_row, int k,
                             const uint8_t* pw1, const uint8_t* pw1s, uint16_t* act, int H, int F, int P_local,
                             hipStream_t st) {
-  const unsigned grid = (unsigned)(P_local * (F / kA16Cols));
+  const unsigned grid = (unsigned)(P_local * (F / a16_cols<true>()));
   k_gemm_a16<true><<<grid, 256, 0, st>>>(x, (uint32_t)((size_t)T * H * 2), offsets, pair_of_row, k, pw1, pw1s, act,
                                          nullptr, H, F);
   return hipGetLastError();
@@ -178,7 +163,7 @@ hipError_t launch_gemm1_a16(const uint16_t* x, int T, const int32_t* offsets, co
 
 hipError_t launch_gemm2_a16(const uint16_t* act, int rows_max, const int32_t* offsets, const uint8_t* pw2,
                             const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
-  const unsigned grid = (unsigned)(P_local * (H / kA16Cols));
+  const unsigned grid = (unsigned)(P_local * ((H + a16_cols<false>() - 1) / a16_cols<false>()));
   k_gemm_a16<false><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)rows_max * F * 2), offsets, nullptr, 1, pw2, pw2s,
                                           nullptr, y, H, F);
   return hipGetLastError();
