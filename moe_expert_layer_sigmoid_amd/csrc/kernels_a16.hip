@@ -112,7 +112,8 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
       for (int i = 0; i < 2; ++i) {
         v4i a[NW], b[4];
 #pragma unroll
-        for (int j = 0; j < NW; ++j) a[j] = *reinterpret_cast<const v4i*>(wd[j] + (size_t)st * 2048 + i * 1024);
+        for (int j = 0; j < NW; ++j)  // streamed once per call: non-temporal
+          a[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wd[j] + (size_t)st * 2048 + i * 1024));
         const int col = (8 * st + 4 * i + g) * 32;  // this lane's block, in elements
         // blocks past K (padding of the packed layout) take zeros
         const uint32_t o = col < K ? boff + (uint32_t)col * 2u : src_bytes;
