@@ -245,12 +245,16 @@ int moe_forward(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, cons
  * act = silu(gate) * up rounded to bf16 (nearest even), GEMM2 on the bf16
  * act, combine as moe_forward.  The weight scale bytes of non-zero MXFP4
  * elements must lie in [2, 252] (every value then a normal bf16; the caller's
- * contract like finite inputs).  taps (nullable): topk_ids, topk_w, phys_ids,
- * counts, offsets, row_of_pair, pair_of_row as moe_forward (other members
- * ignored); act_tap (nullable, device): bf16 act rows [T_max*k, F] in bucket
- * order.  Workspace: moe_a16w4_workspace_bytes(dims).  T * H * 2 and
- * T_max * k * F * 2 bytes must stay below 2^31 (else MOE_ERR_UNSUPPORTED).
- * Seven launches on `stream`. */
+ * contract like finite inputs).  Rows: T <= 1024 takes pair-indexed rows as
+ * MOE_PATH_SMALL_M (four launches), larger T bucketed rows as the staged
+ * path (seven launches).  taps (nullable): topk_ids, topk_w, phys_ids,
+ * counts, offsets as moe_forward, and for bucketed rows also row_of_pair,
+ * pair_of_row (other members ignored); act_tap (nullable, device): bf16 act
+ * rows [T_max*k, F], in bucket order for bucketed rows, by pair t*k+j for
+ * pair-indexed rows (rows of remote pairs unspecified).  Workspace:
+ * moe_a16w4_workspace_bytes(dims).  T * H * 2 and T_max * k * F * 2 bytes
+ * must stay below 2^31 (else MOE_ERR_UNSUPPORTED).  Asynchronous on
+ * `stream`. */
 size_t moe_a16w4_workspace_bytes(const moe_dims_t* dims);
 int moe_forward_a16w4(const moe_dims_t* dims, const uint16_t* x, const float* logits, const uint8_t* pw1,
                       const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rep_count,

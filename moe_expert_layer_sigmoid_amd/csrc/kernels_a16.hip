@@ -23,6 +23,7 @@
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 #include "moe_layout.hpp"
+#include "moe_pairs.hpp"
 
 namespace moe {
 namespace {
@@ -60,19 +61,35 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
 
 // G1: h = W1 x (bf16 input rows of the slot's pairs), act = bf16(silu(gate) up)
 // into act rows [rows, F].  G2: y = W2 act into y rows [rows, H] (f32).
-template <bool G1>
+// Bucketed (PAIRS false): the slot's rows are [offsets[s], offsets[s+1]), row r
+// of token pair_of_row[r] / k.  Pair-indexed (PAIRS true): the block lists the
+// pairs p with phys[p] == p0 + s (ascending) itself; act and y rows are pair
+// rows [T k, .], the token of pair p is p / k, and GEMM1 writes the slot's
+// pair count into counts[s].
+template <bool G1, bool PAIRS>
 __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ src, uint32_t src_bytes,
                                                  const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ pair_of_row, int k,
+                                                 const int32_t* __restrict__ pair_of_row,
+                                                 const int32_t* __restrict__ phys, int np, int p0,
+                                                 int32_t* __restrict__ counts, int k,
                                                  const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws,
                                                  uint16_t* __restrict__ act, float* __restrict__ y, int H, int F) {
+  __shared__ int s_list[PAIRS ? kPairMaxT : 1];
+  __shared__ int s_cnt[2][4];
   constexpr int NW = 4;  // weight tiles per wave
   constexpr int kA16Cols = a16_cols<G1>(), WC = kA16Cols / 4;  // columns per block / wave
   const int K = G1 ? H : F, R = G1 ? 2 * F : H, ncol = G1 ? F : H;
   const int nfb = (ncol + kA16Cols - 1) / kA16Cols;
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nfb, fb = item - s * nfb;
-  const int row0 = offsets[s], n = offsets[s + 1] - row0;
+  int row0 = 0, n;
+  if (PAIRS) {
+    n = slot_pairs(phys, np, p0 + s, s_list, kPairMaxT, s_cnt);  // block-wide (barriers)
+    if (G1 && fb == 0 && threadIdx.x == 0) counts[s] = n;
+  } else {
+    row0 = offsets[s];
+    n = offsets[s + 1] - row0;
+  }
   if (n <= 0) return;  // block-uniform: an idle expert reads no weights
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
@@ -95,8 +112,11 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
     const int rr = tt + r16;
     const bool valid = rr < n;
     uint32_t boff = src_bytes;  // past the buffer: zeros
+    int orow_i = 0;
     if (valid) {
-      const int srow = G1 ? pair_of_row[row0 + rr] / k : row0 + rr;
+      const int pr = PAIRS ? s_list[rr] : (G1 ? pair_of_row[row0 + rr] : row0 + rr);
+      orow_i = PAIRS ? pr : row0 + rr;
+      const int srow = G1 ? pr / k : (PAIRS ? pr : row0 + rr);
       boff = (uint32_t)srow * (uint32_t)K * 2u;
     }
     v4f acc[NW];
@@ -131,7 +151,7 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
     }
     if (!valid) continue;
     // lane (g, r16) holds rows 4 g + q of each weight tile for token row rr
-    const size_t orow = (size_t)(row0 + rr);
+    const size_t orow = (size_t)orow_i;
     if (G1) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {  // columns c0 + 16 u + 4 g + [0, 4)
@@ -157,16 +177,33 @@ hipError_t launch_gemm1_a16(const uint16_t* x, int T, const int32_t* offsets, co
                             const uint8_t* pw1, const uint8_t* pw1s, uint16_t* act, int H, int F, int P_local,
                             hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * (F / a16_cols<true>()));
-  k_gemm_a16<true><<<grid, 256, 0, st>>>(x, (uint32_t)((size_t)T * H * 2), offsets, pair_of_row, k, pw1, pw1s, act,
-                                         nullptr, H, F);
+  k_gemm_a16<true, false><<<grid, 256, 0, st>>>(x, (uint32_t)((size_t)T * H * 2), offsets, pair_of_row, nullptr, 0, 0,
+                                                nullptr, k, pw1, pw1s, act, nullptr, H, F);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_a16(const uint16_t* act, int rows_max, const int32_t* offsets, const uint8_t* pw2,
                             const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * ((H + a16_cols<false>() - 1) / a16_cols<false>()));
-  k_gemm_a16<false><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)rows_max * F * 2), offsets, nullptr, 1, pw2, pw2s,
-                                          nullptr, y, H, F);
+  k_gemm_a16<false, false><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)rows_max * F * 2), offsets, nullptr, nullptr,
+                                                 0, 0, nullptr, 1, pw2, pw2s, nullptr, y, H, F);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm1_a16_pairs(const uint16_t* x, int T, int k, const int32_t* phys, int p0, const uint8_t* pw1,
+                                  const uint8_t* pw1s, uint16_t* act, int32_t* counts, int H, int F, int P_local,
+                                  hipStream_t st) {
+  const unsigned grid = (unsigned)(P_local * (F / a16_cols<true>()));
+  k_gemm_a16<true, true><<<grid, 256, 0, st>>>(x, (uint32_t)((size_t)T * H * 2), nullptr, nullptr, phys, T * k, p0,
+                                               counts, k, pw1, pw1s, act, nullptr, H, F);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_a16_pairs(const uint16_t* act, int T, int k, const int32_t* phys, int p0, const uint8_t* pw2,
+                                  const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
+  const unsigned grid = (unsigned)(P_local * ((H + a16_cols<false>() - 1) / a16_cols<false>()));
+  k_gemm_a16<false, true><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)T * k * F * 2), nullptr, nullptr, phys, T * k,
+                                                p0, nullptr, 1, pw2, pw2s, nullptr, y, H, F);
   return hipGetLastError();
 }
 

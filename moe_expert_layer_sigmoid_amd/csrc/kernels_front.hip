@@ -568,7 +568,8 @@ hipError_t launch_front(int T, int E, int k, int H, const float* logits, const u
                         hipStream_t st, const int32_t* t_dev) {
   if (T == 0) return hipSuccess;
   const int nr = (T + 15) / 16;
-  const long waves = (long)T * ((H / kActBlock + 3) / 4);
+  // xq_tok == NULL: routing blocks only (callers that take bf16 rows)
+  const long waves = xq_tok ? (long)T * ((H / kActBlock + 3) / 4) : 0;
   const unsigned grid = (unsigned)(nr + (waves + 15) / 16);
   switch (route_epl(E)) {
 #define X(N)                                                                                                   \

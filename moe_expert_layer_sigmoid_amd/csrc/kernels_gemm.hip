@@ -25,6 +25,7 @@
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 #include "moe_layout.hpp"
+#include "moe_pairs.hpp"
 
 namespace moe {
 
@@ -259,59 +260,6 @@ constexpr int kMaxSteps = 64;    // K <= 16384
 constexpr int kWeightAux = 2;
 constexpr int kPairRows = kPairMaxT;  // rows of one slot on the pair-indexed path
 
-// The pairs (t, j) whose physical slot is q, ascending, into list[0, cap);
-// returns their number (the same in every thread).  256 threads; each
-// iteration covers 1024 pairs, four consecutive ones per thread, placed by
-// ballots within a wavefront and by the wavefront totals across the block.
-__device__ __forceinline__ int4 pairs4(const int32_t* __restrict__ phys, int np, int i0) {
-  if (i0 + 3 < np) return *reinterpret_cast<const int4*>(phys + i0);
-  int4 v;
-  v.x = i0 < np ? phys[i0] : -1;
-  v.y = i0 + 1 < np ? phys[i0 + 1] : -1;
-  v.z = i0 + 2 < np ? phys[i0 + 2] : -1;
-  v.w = i0 + 3 < np ? phys[i0 + 3] : -1;
-  return v;
-}
-
-__device__ int slot_pairs(const int32_t* __restrict__ phys, int np, int q, int* list, int cap, int (*s_cnt)[4]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int run = 0, buf = 0;
-  int4 cur = pairs4(phys, np, 4 * tid);
-  for (int base = 0; base < np; base += 1024) {
-    const int i0 = base + 4 * tid;
-    const int4 nxt = base + 1024 < np ? pairs4(phys, np, i0 + 1024) : int4{-1, -1, -1, -1};  // one ahead
-    const int v[4] = {cur.x, cur.y, cur.z, cur.w};
-    int before = 0, total = 0;
-    bool f[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f[m] = v[m] == q;
-      const uint64_t bal = __ballot(f[m]);
-      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-      total += __popcll(bal);
-    }
-    if (lane == 0) s_cnt[buf][wave] = total;
-    __syncthreads();
-    int pos = run + before, all = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int cw = s_cnt[buf][w];
-      pos += w < wave ? cw : 0;
-      all += cw;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if (f[m]) {
-        if (pos < cap) list[pos] = i0 + m;
-        ++pos;
-      }
-    run += all;
-    buf ^= 1;
-    cur = nxt;
-  }
-  __syncthreads();  // the list is complete
-  return run;
-}
 
 // Stage the token tiles' 128-column scales in LDS: `rows` rows of 2 * S4
 // bytes, zero beyond K/128 (padded steps) and beyond the tiles' rows.

@@ -465,8 +465,20 @@ int moe_forward_a16w4(const moe_dims_t* d, const uint16_t* x, const float* logit
   int32_t* partial = at<int32_t>(ws, L.partial);
   int32_t* base = at<int32_t>(ws, L.base);
   float* y = at<float>(ws, L.y);
-  // routing, remap + record, buckets as in the a8w4 layer; the row maps come
-  // from the bucketed quantise kernel (its fp8 rows are not used here)
+  if (d->T <= kPairMaxT) {
+    // pair-indexed rows as the a8w4 small-input path: the fused front (routing
+    // and remap only), GEMMs listing their slot's pairs, combine + record
+    MOE_TRY(launch_front(d->T, d->E, d->k, d->H, logits, x, rep_count, rep_slots, d->R_max, d->token_id_base,
+                         d->P_total, ids, w, phys, partial, nullptr, nullptr, st));
+    MOE_TRY(launch_gemm1_a16_pairs(x, d->T, d->k, phys, d->p0, pw1, pw1s, act, counts, d->H, d->F, d->P_local, st));
+    MOE_TRY(launch_gemm2_a16_pairs(act, d->T, d->k, phys, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local, st));
+    MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys, d->p0, d->P_local, w, out, partial,
+                                 (d->T + kFrontTokens - 1) / kFrontTokens, d->P_total, load_hist, counts, offsets,
+                                 st));
+    return MOE_OK;
+  }
+  // bucketed rows: routing, remap + record, buckets as in the a8w4 layer; the
+  // row maps come from the bucketed quantise kernel (its fp8 rows unused)
   MOE_TRY(launch_route(logits, d->T, d->E, d->k, ids, w, st));
   MOE_TRY(launch_count(d->T, d->k, ids, rep_count, rep_slots, d->R_max, d->token_id_base, phys, true, d->P_total,
                        d->p0, d->P_local, partial, rank, st));

@@ -35,6 +35,7 @@ hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* ro
 // chunk counts partial[ceil(T/16), P_total], and every token quantised into
 // xq_tok [T, H] / xs_tok [T, H/128].  t_dev (nullable, device): a token count
 // read on the device; tokens from min(*t_dev, T) on get phys = -1 (idle).
+// xq_tok == NULL: no quantisation blocks (xs_tok ignored).
 constexpr int kFrontTokens = 16;
 hipError_t launch_front(int T, int E, int k, int H, const float* logits, const uint16_t* x, const int32_t* rep_count,
                         const int32_t* rep_slots, int R_max, uint32_t token_id_base, int P_total, int32_t* ids,
@@ -119,5 +120,12 @@ hipError_t launch_gemm1_a16(const uint16_t* x, int T, const int32_t* offsets, co
                             hipStream_t st);
 hipError_t launch_gemm2_a16(const uint16_t* act, int rows_max, const int32_t* offsets, const uint8_t* pw2,
                             const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
+// The same on pair-indexed rows (T <= kPairMaxT): act [T k, F] and y [T k, H]
+// by pair, each block listing its slot's pairs from phys; GEMM1 writes counts.
+hipError_t launch_gemm1_a16_pairs(const uint16_t* x, int T, int k, const int32_t* phys, int p0, const uint8_t* pw1,
+                                  const uint8_t* pw1s, uint16_t* act, int32_t* counts, int H, int F, int P_local,
+                                  hipStream_t st);
+hipError_t launch_gemm2_a16_pairs(const uint16_t* act, int T, int k, const int32_t* phys, int p0, const uint8_t* pw2,
+                                  const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
 
 }  // namespace moe

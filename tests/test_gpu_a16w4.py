@@ -1,6 +1,8 @@
 """GPU parity of the a16w4 variant (moe_forward_a16w4: bf16 activations on the
 MXFP4 experts) against the oracle.
 
+Up to 1024 tokens the variant takes pair-indexed rows (act rows by pair),
+above that bucketed rows; both are compared through the bucket view.
 Bit-exact: routing, remap, histogram, buckets and row maps.  The bf16 act
 rows: every GPU value must be the bf16 rounding of some value within the f32
 accumulation bound of the float64 act (2^-14 of the sum of absolute products,
@@ -24,6 +26,7 @@ from tests.test_gpu_parity import _say
 pytestmark = pytest.mark.gpu
 
 ACC_REL = 2.0 ** -14
+PAIR_MAX_T = 1024  # up to this many tokens the variant takes pair-indexed rows
 
 
 def _run(wl, buf=None):
@@ -45,11 +48,22 @@ def _run(wl, buf=None):
     torch.cuda.synchronize()
     c = {n: v.cpu().numpy() for n, v in taps.items()}
     rows = int(c["offsets"][d.P_local]) if d.T else 0
+    act_np = act.cpu().numpy().view(np.uint16)
+    if d.T <= PAIR_MAX_T:
+        # pair-indexed rows; their bucket view follows from the GPU's own phys:
+        # slot s's rows are its pairs in ascending (t, j) order
+        phys = c["phys_ids"][:TK]
+        por = np.concatenate([np.nonzero(phys == d.p0 + s)[0] for s in range(d.P_local)] +
+                             [np.zeros(0, np.int64)]).astype(np.int32)
+        rop = np.full(TK, -1, np.int32)
+        rop[por] = np.arange(len(por), dtype=np.int32)
+        act_rows = act_np[por]
+    else:
+        rop, por, act_rows = c["row_of_pair"][:TK], c["pair_of_row"][:rows], act_np[:rows]
     return dict(out=out.cpu().numpy().view(np.uint16)[:d.T], hist=hist.cpu().numpy(),
                 topk_ids=c["topk_ids"][:TK].reshape(d.T, d.k), topk_w=c["topk_w"][:TK].reshape(d.T, d.k),
                 phys_ids=c["phys_ids"][:TK].reshape(d.T, d.k), counts=c["counts"], offsets=c["offsets"],
-                row_of_pair=c["row_of_pair"][:TK], pair_of_row=c["pair_of_row"][:rows],
-                act=act.cpu().numpy().view(np.uint16)[:rows])
+                row_of_pair=rop, pair_of_row=por, act=act_rows)
 
 
 def _front(res, ref, d):
@@ -139,6 +153,11 @@ def test_a16w4_ragged_remote_and_padded_k():
 def test_a16w4_many_rows_per_slot():
     # ~100 rows per slot: several 16-row passes per block
     _full(synth.make_custom(T=400, H=256, F=256, E=8, k=2, P_local=8, seed=78))
+
+
+def test_a16w4_bucketed_rows_above_1024_tokens():
+    # 1100 tokens: bucketed rows (route, count, scan, row maps), ragged tail
+    _full(synth.make_custom(T=1100, H=256, F=256, E=16, k=2, P_local=12, p0=2, redundant=2, ranks=2, seed=81))
 
 
 def test_a16w4_single_token_and_all_remote():
