@@ -27,7 +27,8 @@ FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, published
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = ("moe_expert_layer_sigmoid_amd/csrc/kernels_gemm.hip",
                 "moe_expert_layer_sigmoid_amd/csrc/moe_device.hpp",
-                "moe_expert_layer_sigmoid_amd/csrc/moe_layout.hpp")
+                "moe_expert_layer_sigmoid_amd/csrc/moe_layout.hpp",
+                "moe_expert_layer_sigmoid_amd/csrc/moe_pairs.hpp")
 
 
 def _src_hash(paths) -> str:

@@ -62,16 +62,18 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
 // G1: h = W1 x (bf16 input rows of the slot's pairs), act = bf16(silu(gate) up)
 // into act rows [rows, F].  G2: y = W2 act into y rows [rows, H] (f32).
 // Bucketed (PAIRS false): the slot's rows are [offsets[s], offsets[s+1]), row r
-// of token pair_of_row[r] / k.  Pair-indexed (PAIRS true): the block lists the
-// pairs p with phys[p] == p0 + s (ascending) itself; act and y rows are pair
-// rows [T k, .], the token of pair p is p / k, and GEMM1 writes the slot's
-// pair count into counts[s].
+// of token pair_of_row[r] / k.  Pair-indexed (PAIRS true): act and y rows are
+// pair rows [T k, .], the token of pair p is p / k; GEMM1 lists the pairs p
+// with phys[p] == p0 + s (ascending) itself and the slot's first block leaves
+// their count in counts[s] and the list at plist + s * stride, which GEMM2
+// reads.
 template <bool G1, bool PAIRS>
 __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ src, uint32_t src_bytes,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ pair_of_row,
                                                  const int32_t* __restrict__ phys, int np, int p0,
-                                                 int32_t* __restrict__ counts, int k,
+                                                 int32_t* __restrict__ counts, int32_t* __restrict__ plist,
+                                                 int stride, int k,
                                                  const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws,
                                                  uint16_t* __restrict__ act, float* __restrict__ y, int H, int F) {
   __shared__ int s_list[PAIRS ? kPairMaxT : 1];
@@ -83,9 +85,16 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nfb, fb = item - s * nfb;
   int row0 = 0, n;
-  if (PAIRS) {
-    n = slot_pairs(phys, np, p0 + s, s_list, kPairMaxT, s_cnt);  // block-wide (barriers)
-    if (G1 && fb == 0 && threadIdx.x == 0) counts[s] = n;
+  if (PAIRS && G1) {
+    n = min(slot_pairs(phys, np, p0 + s, s_list, kPairMaxT, s_cnt), kPairMaxT);  // block-wide (barriers)
+    if (fb == 0) {
+      if (threadIdx.x == 0) counts[s] = n;
+      for (int i = threadIdx.x; i < n; i += blockDim.x) plist[(size_t)s * stride + i] = s_list[i];
+    }
+  } else if (PAIRS) {
+    n = min(counts[s], kPairMaxT);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) s_list[i] = plist[(size_t)s * stride + i];
+    __syncthreads();
   } else {
     row0 = offsets[s];
     n = offsets[s + 1] - row0;
@@ -178,7 +187,7 @@ hipError_t launch_gemm1_a16(const uint16_t* x, int T, const int32_t* offsets, co
                             hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * (F / a16_cols<true>()));
   k_gemm_a16<true, false><<<grid, 256, 0, st>>>(x, (uint32_t)((size_t)T * H * 2), offsets, pair_of_row, nullptr, 0, 0,
-                                                nullptr, k, pw1, pw1s, act, nullptr, H, F);
+                                                nullptr, nullptr, 0, k, pw1, pw1s, act, nullptr, H, F);
   return hipGetLastError();
 }
 
@@ -186,24 +195,26 @@ hipError_t launch_gemm2_a16(const uint16_t* act, int rows_max, const int32_t* of
                             const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * ((H + a16_cols<false>() - 1) / a16_cols<false>()));
   k_gemm_a16<false, false><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)rows_max * F * 2), offsets, nullptr, nullptr,
-                                                 0, 0, nullptr, 1, pw2, pw2s, nullptr, y, H, F);
+                                                 0, 0, nullptr, nullptr, 0, 1, pw2, pw2s, nullptr, y, H, F);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm1_a16_pairs(const uint16_t* x, int T, int k, const int32_t* phys, int p0, const uint8_t* pw1,
-                                  const uint8_t* pw1s, uint16_t* act, int32_t* counts, int H, int F, int P_local,
-                                  hipStream_t st) {
+                                  const uint8_t* pw1s, uint16_t* act, int32_t* counts, int32_t* plist, int stride,
+                                  int H, int F, int P_local, hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * (F / a16_cols<true>()));
   k_gemm_a16<true, true><<<grid, 256, 0, st>>>(x, (uint32_t)((size_t)T * H * 2), nullptr, nullptr, phys, T * k, p0,
-                                               counts, k, pw1, pw1s, act, nullptr, H, F);
+                                               counts, plist, stride, k, pw1, pw1s, act, nullptr, H, F);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2_a16_pairs(const uint16_t* act, int T, int k, const int32_t* phys, int p0, const uint8_t* pw2,
-                                  const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
+hipError_t launch_gemm2_a16_pairs(const uint16_t* act, int T, int k, const int32_t* counts, const int32_t* plist,
+                                  int stride, const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F,
+                                  int P_local, hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * ((H + a16_cols<false>() - 1) / a16_cols<false>()));
-  k_gemm_a16<false, true><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)T * k * F * 2), nullptr, nullptr, phys, T * k,
-                                                p0, nullptr, 1, pw2, pw2s, nullptr, y, H, F);
+  k_gemm_a16<false, true><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)T * k * F * 2), nullptr, nullptr, nullptr, 0,
+                                                0, const_cast<int32_t*>(counts), const_cast<int32_t*>(plist), stride,
+                                                1, pw2, pw2s, nullptr, y, H, F);
   return hipGetLastError();
 }
 

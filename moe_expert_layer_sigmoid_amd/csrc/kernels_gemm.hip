@@ -302,6 +302,22 @@ __device__ __forceinline__ SlotRows<PAIRS> slot_rows(const int32_t* offsets, con
   return R;
 }
 
+// Pair-indexed GEMM2: the slot's pair list as GEMM1 left it (counts[s]
+// entries, at most kPairRows, at plist + s * stride), staged in LDS.
+template <bool PAIRS>
+__device__ __forceinline__ SlotRows<PAIRS> listed_rows(const int32_t* counts, const int32_t* plist, int stride, int s,
+                                                       int* list) {
+  SlotRows<PAIRS> R;
+  R.div = 1;
+  R.row0 = 0;
+  R.list = list;
+  R.n = min(counts[s], kPairRows);
+  const int32_t* src = plist + (size_t)s * stride;
+  for (int i = threadIdx.x; i < R.n; i += blockDim.x) list[i] = src[i];
+  __syncthreads();
+  return R;
+}
+
 // The token operand of NT 16-row tiles (rows tt0 .. tt0 + nrow - 1 of the
 // slot): a buffer over the input rows and this lane's byte offsets.  Lanes
 // past the rows read zeros (an offset past the buffer); their results are
@@ -328,7 +344,9 @@ __device__ __forceinline__ void token_operand(SOps<NT>& O, const uint8_t* x, con
 // columns is reduced across the four waves in LDS.
 //   bucketed (PAIRS false): xq/xs rows and aq/as rows from `offsets`;
 //   pair-indexed (PAIRS true): xq/xs are per-token rows [nsrc = T], aq/as
-//   per-pair rows [T*k]; the slot's pairs come from phys[0, np).
+//   per-pair rows [T*k]; the slot's pairs come from phys[0, np), and the
+//   slot's first block leaves its count in counts[s] and (plist non-null)
+//   its list at plist + s * stride for GEMM2.
 // ---------------------------------------------------------------------------
 // NT 16-row token tiles share each pass over the block's weights (a slot
 // with more rows streams its weights once per 16 NT rows); NT = 2 needs more
@@ -338,7 +356,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm1_stream(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ phys, int np, int k, int p0, int nsrc, const uint8_t* __restrict__ pw1,
     const uint8_t* __restrict__ pw1s, uint8_t* __restrict__ aq, uint8_t* __restrict__ as_,
-    int32_t* __restrict__ counts, int H, int F) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ plist, int stride, int H, int F) {
   constexpr int kRows = 16 * NT;  // token rows per pass
   __shared__ float s_amax[4][kRows];
   __shared__ __align__(16) uint8_t s_xs[kRows * 2 * kMaxSteps];
@@ -349,7 +367,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm1_stream(
   const int s = item / nfb, fb = item - s * nfb;
   const SlotRows<PAIRS> R = slot_rows<PAIRS>(offsets, phys, np, p0 + s, s, k, s_list, s_cnt);
   const int n = R.n;
-  if (PAIRS && fb == 0 && threadIdx.x == 0) counts[s] = n;
+  if (PAIRS && fb == 0) {
+    if (threadIdx.x == 0) counts[s] = n;
+    if (plist)
+      for (int i = threadIdx.x; i < n; i += blockDim.x) plist[(size_t)s * stride + i] = s_list[i];
+  }
   if (n <= 0) return;  // block-uniform: an idle expert reads no weights
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -421,14 +443,16 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm1_stream(
 // slots = 1344 blocks at three per CU: blocks of 512 rows (two groups per wave,
 // one round over the chip) measured 5-8% slower at 512-1536 tokens.  y rows
 // are f32 [rows, H] (bucketed rows, or pair rows with the act rows
-// pair-indexed too).
+// pair-indexed too; the slot's pairs then come from GEMM1's counts and lists,
+// or with plist null from phys as in GEMM1).
 // ---------------------------------------------------------------------------
 constexpr int kG2Rows = 256;  // rows of H per block
 
 template <bool PAIRS, int NT>
 __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ phys, int np, int p0, int nsrc, const uint8_t* __restrict__ pw2,
+    const int32_t* __restrict__ phys, int np, int p0, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ plist, int stride, int nsrc, const uint8_t* __restrict__ pw2,
     const uint8_t* __restrict__ pw2s, float* __restrict__ y, int H, int F) {
   constexpr int kRows = 16 * NT;  // token rows per pass
   __shared__ __align__(16) uint8_t s_xs[kRows * 2 * kMaxSteps];
@@ -437,7 +461,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
   const int nhb = (H + kG2Rows - 1) / kG2Rows;
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int s = item / nhb, hb = item - s * nhb;
-  const SlotRows<PAIRS> R = slot_rows<PAIRS>(offsets, phys, np, p0 + s, s, 1, s_list, s_cnt);
+  const SlotRows<PAIRS> R = (PAIRS && plist) ? listed_rows<PAIRS>(counts, plist, stride, s, s_list)
+                                             : slot_rows<PAIRS>(offsets, phys, np, p0 + s, s, 1, s_list, s_cnt);
   const int n = R.n;
   if (n <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -494,46 +519,51 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
                                hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * (F / kActBlock));
   if (nt >= 2)
-    k_gemm1_stream<false, 2><<<grid, 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s, aq, as, nullptr, H, F);
+    k_gemm1_stream<false, 2><<<grid, 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s, aq, as, nullptr,
+                                                    nullptr, 0, H, F);
   else
-    k_gemm1_stream<false, 1><<<grid, 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s, aq, as, nullptr, H, F);
+    k_gemm1_stream<false, 1><<<grid, 256, 0, st>>>(xq, xs, offsets, nullptr, 0, 1, 0, 0, pw1, pw1s, aq, as, nullptr,
+                                                    nullptr, 0, H, F);
   return hipGetLastError();
 }
 
 template <bool PAIRS>
 static void gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const int32_t* phys, int np,
-                         int p0, int nsrc, const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F,
-                         int P_local, int nt, hipStream_t st) {
+                         int p0, const int32_t* counts, const int32_t* plist, int stride, int nsrc, const uint8_t* pw2,
+                         const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * ((H + kG2Rows - 1) / kG2Rows));
   if (nt >= 2)
-    k_gemm2_stream<PAIRS, 2><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, nsrc, pw2, pw2s, y, H, F);
+    k_gemm2_stream<PAIRS, 2><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, counts, plist, stride, nsrc, pw2,
+                                                    pw2s, y, H, F);
   else
-    k_gemm2_stream<PAIRS, 1><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, nsrc, pw2, pw2s, y, H, F);
+    k_gemm2_stream<PAIRS, 1><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, counts, plist, stride, nsrc, pw2,
+                                                    pw2s, y, H, F);
 }
 
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                                const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
-  gemm2_stream<false>(aq, as, offsets, nullptr, 0, 0, 0, pw2, pw2s, y, H, F, P_local, nt, st);
+  gemm2_stream<false>(aq, as, offsets, nullptr, 0, 0, nullptr, nullptr, 0, 0, pw2, pw2s, y, H, F, P_local, nt, st);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int32_t* counts,
-                              int H, int F, int P_local, int nt, hipStream_t st) {
+                              int32_t* plist, int stride, int H, int F, int P_local, int nt, hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * (F / kActBlock));
   if (nt >= 2)
     k_gemm1_stream<true, 2><<<grid, 256, 0, st>>>(xq_tok, xs_tok, nullptr, phys, T * k, k, p0, T, pw1, pw1s, aq, as,
-                                                   counts, H, F);
+                                                   counts, plist, stride, H, F);
   else
     k_gemm1_stream<true, 1><<<grid, 256, 0, st>>>(xq_tok, xs_tok, nullptr, phys, T * k, k, p0, T, pw1, pw1s, aq, as,
-                                                   counts, H, F);
+                                                   counts, plist, stride, H, F);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
-                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt,
-                              hipStream_t st) {
-  gemm2_stream<true>(aq, as, nullptr, phys, T * k, p0, T * k, pw2, pw2s, y, H, F, P_local, nt, st);
+                              const int32_t* counts, const int32_t* plist, int stride, const uint8_t* pw2,
+                              const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
+  gemm2_stream<true>(aq, as, nullptr, phys, T * k, p0, counts, plist, stride, T * k, pw2, pw2s, y, H, F, P_local, nt,
+                     st);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, phys, rank, partial, base, counts, offsets, rop, por, xq, xs, aq, as, y, total;
+  size_t ids, w, phys, rank, partial, base, counts, offsets, rop, por, xq, xs, aq, as, y, plist, total;
 };
 
 // One workspace serves every call; regions are sized by T_max.
@@ -48,6 +48,8 @@ Layout layout_of(const moe_dims_t* d) {
   L.aq = take(TK * d->F);
   L.as = take(TK * (d->F / kActBlock));
   L.y = take(TK * d->H * 4);
+  // per-slot pair lists of the pair-indexed GEMMs (GEMM1 -> GEMM2)
+  L.plist = take((size_t)d->P_local * pair_list_stride(d->T_max, d->k) * 4);
   L.total = off;
   return L;
 }
@@ -274,7 +276,8 @@ int moe_grouped_gemm1_swiglu_pairs(const moe_dims_t* d, const uint8_t* xq_tok, c
   if (d->T > kPairMaxT) return MOE_ERR_UNSUPPORTED;
   if (d->T == 0) return MOE_OK;
   return hip_status(launch_gemm1_pairs(xq_tok, xs_tok, phys_ids, d->T, d->k, d->p0, pw1, pw1s, aq_pair, as_pair,
-                                       counts, d->H, d->F, d->P_local, stream_tiles(d), (hipStream_t)stream));
+                                       counts, nullptr, 0, d->H, d->F, d->P_local, stream_tiles(d),
+                                       (hipStream_t)stream));
 }
 
 int moe_grouped_gemm2_combine_pairs(const moe_dims_t* d, const uint8_t* aq_pair, const uint8_t* as_pair,
@@ -291,8 +294,8 @@ int moe_grouped_gemm2_combine_pairs(const moe_dims_t* d, const uint8_t* aq_pair,
   if (d->T == 0) return MOE_OK;
   hipStream_t st = (hipStream_t)stream;
   float* y = at<float>(ws, layout_of(d).y);
-  MOE_TRY(launch_gemm2_pairs(aq_pair, as_pair, phys_ids, d->T, d->k, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local,
-                             stream_tiles(d), st));
+  MOE_TRY(launch_gemm2_pairs(aq_pair, as_pair, phys_ids, d->T, d->k, d->p0, nullptr, nullptr, 0, pw2, pw2s, y, d->H,
+                             d->F, d->P_local, stream_tiles(d), st));
   MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys_ids, d->p0, d->P_local, topk_w, out, nullptr, 0,
                                d->P_total, nullptr, counts, offsets, st));
   return MOE_OK;
@@ -360,9 +363,12 @@ int forward_impl(const moe_dims_t* d, moe_path_t path, const int32_t* t_dev, con
     MOE_TRY(launch_front(d->T, d->E, d->k, d->H, logits, x, rep_count, rep_slots, d->R_max, d->token_id_base,
                          d->P_total, ids, w, phys, partial, xq_tok, xs_tok, st, t_dev));
     const int nt = stream_tiles(d);
-    MOE_TRY(launch_gemm1_pairs(xq_tok, xs_tok, phys, d->T, d->k, d->p0, pw1, pw1s, aq_p, as_p, counts, d->H, d->F,
+    int32_t* plist = at<int32_t>(ws, L.plist);
+    const int stride = pair_list_stride(d->T_max, d->k);
+    MOE_TRY(launch_gemm1_pairs(xq_tok, xs_tok, phys, d->T, d->k, d->p0, pw1, pw1s, aq_p, as_p, counts, plist, stride,
+                               d->H, d->F, d->P_local, nt, st));
+    MOE_TRY(launch_gemm2_pairs(aq_p, as_p, phys, d->T, d->k, d->p0, counts, plist, stride, pw2, pw2s, y, d->H, d->F,
                                d->P_local, nt, st));
-    MOE_TRY(launch_gemm2_pairs(aq_p, as_p, phys, d->T, d->k, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local, nt, st));
     MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys, d->p0, d->P_local, w, out, partial,
                                  (d->T + kFrontTokens - 1) / kFrontTokens, d->P_total, load_hist, counts, offsets,
                                  st));
@@ -470,8 +476,11 @@ int moe_forward_a16w4(const moe_dims_t* d, const uint16_t* x, const float* logit
     // and remap only), GEMMs listing their slot's pairs, combine + record
     MOE_TRY(launch_front(d->T, d->E, d->k, d->H, logits, x, rep_count, rep_slots, d->R_max, d->token_id_base,
                          d->P_total, ids, w, phys, partial, nullptr, nullptr, st));
-    MOE_TRY(launch_gemm1_a16_pairs(x, d->T, d->k, phys, d->p0, pw1, pw1s, act, counts, d->H, d->F, d->P_local, st));
-    MOE_TRY(launch_gemm2_a16_pairs(act, d->T, d->k, phys, d->p0, pw2, pw2s, y, d->H, d->F, d->P_local, st));
+    int32_t* plist = at<int32_t>(ws, L.plist);
+    const int stride = pair_list_stride(d->T_max, d->k);
+    MOE_TRY(launch_gemm1_a16_pairs(x, d->T, d->k, phys, d->p0, pw1, pw1s, act, counts, plist, stride, d->H, d->F,
+                                   d->P_local, st));
+    MOE_TRY(launch_gemm2_a16_pairs(act, d->T, d->k, counts, plist, stride, pw2, pw2s, y, d->H, d->F, d->P_local, st));
     MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys, d->p0, d->P_local, w, out, partial,
                                  (d->T + kFrontTokens - 1) / kFrontTokens, d->P_total, load_hist, counts, offsets,
                                  st));

@@ -59,17 +59,24 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
                                hipStream_t st);
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                                const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st);
-// Pair-indexed GEMMs: each block lists its slot's pairs from phys [T*k].
-// GEMM1 reads per-token rows xq_tok/xs_tok and writes pair rows aq/as
+// Pair-indexed GEMMs: GEMM1's blocks list their slot's pairs from phys
+// [T*k], read per-token rows xq_tok/xs_tok and write pair rows aq/as
 // [T*k, F]; GEMM2 reads those and writes pair rows y [T*k, H].  T <= 1024.
 constexpr int kPairMaxT = 1024;
-// GEMM1 also writes each slot's pair count into counts [P_local].
+// GEMM1 also leaves each slot's pair count in counts [P_local] and (plist
+// non-null) its pair list at plist + s * stride (stride =
+// pair_list_stride(T_max, k)), which GEMM2 takes instead of listing the
+// pairs from phys again (with plist null GEMM2 lists them itself).
+inline int pair_list_stride(int T_max, int k) {
+  const long tk = (long)T_max * k;
+  return (int)(tk < kPairMaxT ? tk : kPairMaxT);
+}
 hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int32_t* counts,
-                              int H, int F, int P_local, int nt, hipStream_t st);
+                              int32_t* plist, int stride, int H, int F, int P_local, int nt, hipStream_t st);
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
-                              const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt,
-                              hipStream_t st);
+                              const int32_t* counts, const int32_t* plist, int stride, const uint8_t* pw2,
+                              const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st);
 // Large-M: persistent tiled kernels.  Their LDS (operand rings plus the
 // block's token scales) must fit a CU's 160 KB, which holds for
 // H, F <= 8192: tiled_fits(H, F, P_local).
@@ -121,11 +128,13 @@ hipError_t launch_gemm1_a16(const uint16_t* x, int T, const int32_t* offsets, co
 hipError_t launch_gemm2_a16(const uint16_t* act, int rows_max, const int32_t* offsets, const uint8_t* pw2,
                             const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
 // The same on pair-indexed rows (T <= kPairMaxT): act [T k, F] and y [T k, H]
-// by pair, each block listing its slot's pairs from phys; GEMM1 writes counts.
+// by pair; GEMM1's blocks list their slot's pairs from phys and leave counts
+// and lists as launch_gemm1_pairs does, GEMM2 takes them.
 hipError_t launch_gemm1_a16_pairs(const uint16_t* x, int T, int k, const int32_t* phys, int p0, const uint8_t* pw1,
-                                  const uint8_t* pw1s, uint16_t* act, int32_t* counts, int H, int F, int P_local,
-                                  hipStream_t st);
-hipError_t launch_gemm2_a16_pairs(const uint16_t* act, int T, int k, const int32_t* phys, int p0, const uint8_t* pw2,
-                                  const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
+                                  const uint8_t* pw1s, uint16_t* act, int32_t* counts, int32_t* plist, int stride,
+                                  int H, int F, int P_local, hipStream_t st);
+hipError_t launch_gemm2_a16_pairs(const uint16_t* act, int T, int k, const int32_t* counts, const int32_t* plist,
+                                  int stride, const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F,
+                                  int P_local, hipStream_t st);
 
 }  // namespace moe
