@@ -197,16 +197,22 @@ __global__ __launch_bounds__(256) void k_count(int T, int k, const int32_t* __re
     }
   }
   if (rank) {
-    for (int s = threadIdx.x; s < P_local; s += blockDim.x) {
-      const int q = p0 + s;
+    // each local pair counts the earlier pairs of its slot in the chunk: the
+    // wavefront reads the chunk's pairs below its last pair as broadcasts
+    for (int i0 = 0; i0 < np; i0 += blockDim.x) {
+      const int i = i0 + (int)threadIdx.x;
+      const int q = i < np ? s_phys[i] : -1;
+      const bool local = q >= p0 && q < p0 + P_local;
+      const int wmax = min(i0 + ((int)threadIdx.x | 63), np - 1);  // the wavefront's last pair
+      const int n4 = __builtin_amdgcn_readfirstlane((wmax + 4) / 4);
       int r = 0;
-      for (int i = 0; i < np4; ++i) {
-        const int4 v = s_phys4[i];
-        if (v.x == q) rank[pr0 + 4 * i] = r++;
-        if (v.y == q) rank[pr0 + 4 * i + 1] = r++;
-        if (v.z == q) rank[pr0 + 4 * i + 2] = r++;
-        if (v.w == q) rank[pr0 + 4 * i + 3] = r++;
+#pragma unroll 8
+      for (int j = 0; j < n4; ++j) {
+        const int4 v = s_phys4[j];  // same address in every lane: a broadcast
+        const int b = 4 * j;
+        r += (v.x == q && b < i) + (v.y == q && b + 1 < i) + (v.z == q && b + 2 < i) + (v.w == q && b + 3 < i);
       }
+      if (local) rank[pr0 + i] = r;
     }
   }
 }
