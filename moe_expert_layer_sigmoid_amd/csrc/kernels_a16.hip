@@ -212,6 +212,7 @@ hipError_t launch_gemm2_a16_pairs(const uint16_t* act, int T, int k, const int32
                                   int stride, const uint8_t* pw2, const uint8_t* pw2s, float* y, int H, int F,
                                   int P_local, hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * ((H + a16_cols<false>() - 1) / a16_cols<false>()));
+  // the GEMM2 instance only reads counts and plist (the casts are for the shared signature)
   k_gemm_a16<false, true><<<grid, 256, 0, st>>>(act, (uint32_t)((size_t)T * k * F * 2), nullptr, nullptr, nullptr, 0,
                                                 0, const_cast<int32_t*>(counts), const_cast<int32_t*>(plist), stride,
                                                 1, pw2, pw2s, nullptr, y, H, F);
