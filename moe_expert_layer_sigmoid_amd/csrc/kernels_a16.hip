@@ -68,7 +68,7 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
 // their count in counts[s] and the list at plist + s * stride, which GEMM2
 // reads.
 template <bool G1, bool PAIRS>
-__global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ src, uint32_t src_bytes,
+__global__ __launch_bounds__(256, 3) void k_gemm_a16(const uint16_t* __restrict__ src, uint32_t src_bytes,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ pair_of_row,
                                                  const int32_t* __restrict__ phys, int np, int p0,
@@ -106,16 +106,21 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
   if (c0 >= ncol) return;  // wave-uniform (the last GEMM2 block when H % 256 == 128); no barriers below
   const PackGeom G = pack_geom((uint32_t)R, (uint32_t)K);
   const int S4 = (int)G.steps;
-  const uint8_t* wd[NW];
+  // weights through a buffer over the slot's packed data: a load at the
+  // buffer's size (the prefetch past the last K step) reads zeros and no memory
+  const uint32_t wbytes = (uint32_t)G.data_slot;
+  const rsrc_t wr = make_rsrc(pw + (size_t)s * G.data_slot, wbytes);
+  uint32_t wt[NW];
   const uint8_t* wsc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
     // GEMM1: gate tiles of columns c0, c0 + 16, then the matching up tiles
     const int tile = G1 ? (j >= 2 ? F : 0) / 16 + (c0 + 16 * (j & 1)) / 16 : (c0 + 16 * j) / 16;
-    wd[j] = pw + (size_t)s * G.data_slot + (size_t)tile * G.data_tile + lane * 16;
+    wt[j] = (uint32_t)tile * (uint32_t)G.data_tile + (uint32_t)lane * 16u;
     wsc[j] = pws + (size_t)s * G.scale_slot + (size_t)tile * G.scale_tile + lane * 8;
   }
   const rsrc_t xr = make_rsrc(src, src_bytes);
+  const int ng = S4 / 4;  // scale groups of four K steps (S4 is a multiple of 4)
 
   for (int tt = 0; tt < n; tt += 16) {
     const int rr = tt + r16;
@@ -128,35 +133,85 @@ __global__ __launch_bounds__(256) void k_gemm_a16(const uint16_t* __restrict__ s
       const int srow = G1 ? pr / k : (PAIRS ? pr : row0 + rr);
       boff = (uint32_t)srow * (uint32_t)K * 2u;
     }
+    // operands of one half-step h (K step h / 2, half h % 2): the wave's
+    // weight tiles and the token rows; h = 2 S4 (the prefetch past the end)
+    // reads zeros
+    struct Stage {
+      v4i a[NW];
+      v4i b[4];
+    };
+    auto load_stage = [&](Stage& S, int h) {
+      const bool live = h < 2 * S4;
+#pragma unroll
+      for (int j = 0; j < NW; ++j)  // streamed once per call: non-temporal
+        S.a[j] = buf_load16_p<2>(wr, live ? wt[j] : wbytes, live ? (uint32_t)h * 1024u : 0u);
+      const int col = (4 * h + g) * 32;  // this lane's block, in elements
+      // blocks past K (padding of the packed layout, or past the last step) take zeros
+      const uint32_t o = col < K ? boff + (uint32_t)col * 2u : src_bytes;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) S.b[m] = buf_load16(xr, o + 16u * m, 0);
+    };
+    auto load_sc = [&](v2i(&sc)[NW], int grp) {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) sc[j] = *reinterpret_cast<const v2i*>(wsc[j] + (size_t)grp * 512);
+    };
     v4f acc[NW];
 #pragma unroll
     for (int j = 0; j < NW; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-    v2i sc[NW];
-    for (int st = 0; st < S4; ++st) {
-      if ((st & 3) == 0) {
+    // half-step bi (0..7) of the current scale group: scale byte bi of each tile
+    auto mma = [&](const Stage& S, const v2i(&sc)[NW], int bi) {
 #pragma unroll
-        for (int j = 0; j < NW; ++j) sc[j] = *reinterpret_cast<const v2i*>(wsc[j] + (size_t)(st >> 2) * 512);
+      for (int j = 0; j < NW; ++j) {
+        const uint32_t sb = ((uint32_t)(bi < 4 ? sc[j].x : sc[j].y) >> (8 * (bi & 3))) & 0xFFu;
+        const float scale = __uint_as_float(sb << 23);  // 2^(sb - 127); 0 for sb = 0 (zero padding)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[j] = mfma_bf16(expand8((uint32_t)S.a[j][m], scale), S.b[m], acc[j]);
       }
+    };
+    // two half-steps in registers: h + 1 loads while h multiplies
+    Stage s0, s1;
+    v2i scc[NW], scn[NW];
+    load_sc(scc, 0);
+    load_stage(s0, 0);
+    // (scheduling barriers keep each prefetch ahead of the previous stage's
+    // multiplies: the scheduler would otherwise sink the loads and wait early)
+    for (int q = 0; q < ng; ++q) {
+      const int h = 8 * q;
+      load_sc(scn, min(q + 1, ng - 1));
+      load_stage(s1, h + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s0, scc, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(s0, h + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s1, scc, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(s1, h + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s0, scc, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(s0, h + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s1, scc, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(s1, h + 5);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s0, scc, 4);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(s0, h + 6);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s1, scc, 5);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(s1, h + 7);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s0, scc, 6);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(s0, h + 8);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s1, scc, 7);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        v4i a[NW], b[4];
-#pragma unroll
-        for (int j = 0; j < NW; ++j)  // streamed once per call: non-temporal
-          a[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wd[j] + (size_t)st * 2048 + i * 1024));
-        const int col = (8 * st + 4 * i + g) * 32;  // this lane's block, in elements
-        // blocks past K (padding of the packed layout) take zeros
-        const uint32_t o = col < K ? boff + (uint32_t)col * 2u : src_bytes;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) b[m] = buf_load16(xr, o + 16u * m, 0);
-        const int bi = 2 * (st & 3) + i;  // scale byte of this half-step
-#pragma unroll
-        for (int j = 0; j < NW; ++j) {
-          const uint32_t sb = ((uint32_t)(bi < 4 ? sc[j].x : sc[j].y) >> (8 * (bi & 3))) & 0xFFu;
-          const float scale = __uint_as_float(sb << 23);  // 2^(sb - 127); 0 for sb = 0 (zero padding)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) acc[j] = mfma_bf16(expand8((uint32_t)a[j][m], scale), b[m], acc[j]);
-        }
-      }
+      for (int j = 0; j < NW; ++j) scc[j] = scn[j];
     }
     if (!valid) continue;
     // lane (g, r16) holds rows 4 g + q of each weight tile for token row rr
