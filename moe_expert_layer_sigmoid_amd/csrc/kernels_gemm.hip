@@ -184,7 +184,8 @@ __device__ __forceinline__ void s_mma(v4f (&acc)[4][NT], const SStage<NT>& S, co
 // byte offsets g * gd in the data and g * sgd in the scales), streamed back
 // to back: all S4 (a multiple of 4) K steps of group 0, then of group 1, ...
 // Operand stages run two steps ahead and scale quads one quad ahead across
-// group boundaries, so the pipeline never drains between groups; the loop has
+// group boundaries (each quad's scales issued before the previous quad's
+// operand loads), so the pipeline never drains between quads or groups; the loop has
 // no branches (its last loads re-read the final steps and are never used).
 // After a group's last step epi(g, acc) consumes its results and acc restarts
 // at zero.  WAUX: cache policy of the weight loads.
@@ -203,14 +204,19 @@ __device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT>&
     const int g = (G > 1 && q >= nq) ? 1 : 0;
     s_load_scales(C, O, q - g * nq, g ? sgd : 0u);
   };
-  ldsc(c0, 0);
+  ldsc(c1, 0);
   ld(s0, 0);
   ld(s1, 1);
-  ldsc(c1, min(1, NQ - 1));
 #pragma unroll 1
   for (int g = 0; g < G; ++g) {
     for (int q = 0; q < nq; ++q) {
       const int st = 4 * q, v = g * S4 + st, vq = g * nq + q;
+      // this quad's scales, loaded a quad ahead and before that quad's operand
+      // loads: waiting for them (the copy) never waits for operands in flight,
+      // which a scale load issued after them would make it do
+      c0 = c1;
+      ldsc(c1, min(vq + 1, NQ - 1));
+      __builtin_amdgcn_sched_barrier(0);
       int sb0[NT], sb1[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -225,8 +231,6 @@ __device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT>&
       ld(s0, min(v + 4, V - 2));
       s_mma<3>(acc, s1, c0, sb1);
       ld(s1, min(v + 5, V - 1));
-      c0 = c1;
-      ldsc(c1, min(vq + 2, NQ - 1));
     }
     epi(g, acc);
 #pragma unroll
