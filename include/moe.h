@@ -26,7 +26,8 @@
  * Conventions for every call
  *  - Pointers other than `dims`, `taps` and `chosen` are DEVICE pointers owned
  *    by the caller; they must be 16-byte aligned.  The library allocates
- *    nothing and keeps no state between calls.
+ *    nothing and keeps no state between calls (moe_forward_noalloc's scratch
+ *    is a fixed array of the library's device code, not an allocation).
  *  - Every call is asynchronous on `stream` (NULL = the default stream); it
  *    never synchronises the host and never prints.
  *  - Arguments are validated on the host before any launch; a failed check
@@ -79,7 +80,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* null pointer, bad shape or misaligned pointer */
   MOE_ERR_UNSUPPORTED = -2, /* a size beyond the limits below */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_bytes */
-  MOE_ERR_HIP = -4          /* a kernel launch failed */
+  MOE_ERR_HIP = -4,         /* a kernel launch failed */
+  MOE_ERR_SCRATCH = -5      /* moe_forward_noalloc: the dims need more than its fixed scratch */
 } moe_status_t;
 
 typedef enum {
@@ -339,6 +341,26 @@ int moe_eplb_rebalance(int32_t E, int32_t P_total, int32_t n_ranks, int32_t R_ma
 int moe_eplb_migrate(const moe_dims_t* dims, const int32_t* src_expert, int32_t n_pool, const uint8_t* pool_pw1,
                      const uint8_t* pool_pw1s, const uint8_t* pool_pw2, const uint8_t* pool_pw2s, uint8_t* pw1,
                      uint8_t* pw1s, uint8_t* pw2, uint8_t* pw2s, moe_stream_t stream);
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, paths, results and errors as
+ * moe_forward with taps = NULL; the workspace is instead a fixed device
+ * array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, that
+ * each GPU the library runs on holds until the process ends.  The first call
+ * on a device resolves that device's copy (the calling thread's current
+ * device must be the stream's device).  Dims whose moe_workspace_bytes exceed
+ * the scratch return MOE_ERR_SCRATCH before any launch (at d_model 7168,
+ * d_ff 2048, top-6: T_max up to 587 tokens).  The call allocates nothing and
+ * needs no part of the scratch to start at zero (every kernel writes what it
+ * reads), but all calls on one GPU share that GPU's scratch, which keeps the
+ * last call's contents: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int moe_forward_noalloc(const moe_dims_t* dims, moe_path_t path, const uint16_t* x, const float* logits,
+                        const uint8_t* pw1, const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s,
+                        const int32_t* rep_count, const int32_t* rep_slots, int32_t* load_hist, uint16_t* out,
+                        moe_path_t* chosen, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK = 0
-STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspace", -4: "hip"}
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspace", -4: "hip",
+          -5: "dims need more than the fixed scratch of moe_forward_noalloc"}
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 PATHS = {"auto": 0, "small_m": 1, "staged": 2, "large_m": 3}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
@@ -30,7 +32,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_p
            "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
            "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
            "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m",
-           "moe_a16w4_workspace_bytes", "moe_forward_a16w4")
+           "moe_a16w4_workspace_bytes", "moe_forward_a16w4", "moe_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -97,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_small_m.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps), P,
                                           ctypes.c_size_t, P]
         L.moe_forward_small_m.restype = I
+        L.moe_forward_noalloc.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_int), P]
+        L.moe_forward_noalloc.restype = I
         L.moe_a16w4_workspace_bytes.argtypes = [D]
         L.moe_a16w4_workspace_bytes.restype = ctypes.c_size_t
         L.moe_forward_a16w4.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(Taps), P, P,
@@ -314,6 +318,24 @@ def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, 
         ctypes.byref(tp) if tp is not None else None, ctypes.byref(chosen),
         _ptr(ws, "workspace", u8), ws.numel(), _stream(stream))
     _check("moe_forward", rc)
+    return PATH_NAMES[chosen.value]
+
+
+def moe_forward_noalloc(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, out, load_hist=None,
+                        path: str = "auto", stream=None) -> str:
+    """moe_forward without a workspace: the library's fixed per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES) serves instead, so the call allocates nothing.
+    Calls that overlap in time on one GPU share that scratch and race.
+    Returns the path taken."""
+    chosen = ctypes.c_int(-1)
+    rc = lib().moe_forward_noalloc(
+        ctypes.byref(d), PATHS[path], _ptr(x, "x", _bf16(x), d.T * d.H), _ptr(logits, "logits", f32, d.T * d.E),
+        _ptr(pw1, "pw1", u8, moe_packed_bytes(d, 0)), _ptr(pw1s, "pw1s", u8, moe_packed_bytes(d, 1)),
+        _ptr(pw2, "pw2", u8, moe_packed_bytes(d, 2)), _ptr(pw2s, "pw2s", u8, moe_packed_bytes(d, 3)),
+        _ptr(rep_count, "rep_count", i32, d.E), _ptr(rep_slots, "rep_slots", i32, d.E * d.R_max),
+        _ptr(load_hist, "load_hist", i32, d.P_total), _ptr(out, "out", _bf16(out), d.T * d.H),
+        ctypes.byref(chosen), _stream(stream))
+    _check("moe_forward_noalloc", rc)
     return PATH_NAMES[chosen.value]
 
 

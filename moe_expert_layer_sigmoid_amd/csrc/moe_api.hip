@@ -3,6 +3,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
@@ -180,6 +183,7 @@ const char* moe_status_string(int s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported size";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "dims need more workspace than the fixed scratch of moe_forward_noalloc";
     default: return "unknown status";
   }
 }
@@ -501,3 +505,52 @@ int moe_forward_a16w4(const moe_dims_t* d, const uint16_t* x, const float* logit
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of moe_forward: the workspace is a file-scope
+// device array, one copy per GPU, that lives as long as the process.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): its device address is resolved once per device
+// with hipGetSymbolAddress, with that device current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (resolved on the first
+// call there).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_forward_noalloc(const moe_dims_t* d, moe_path_t path, const uint16_t* x, const float* logits,
+                                   const uint8_t* pw1, const uint8_t* pw1s, const uint8_t* pw2, const uint8_t* pw2s,
+                                   const int32_t* rep_count, const int32_t* rep_slots, int32_t* load_hist,
+                                   uint16_t* out, moe_path_t* chosen, moe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (layout_of(d).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return forward_impl(d, path, nullptr, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, load_hist, out,
+                      nullptr, chosen, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}

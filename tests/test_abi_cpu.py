@@ -65,7 +65,7 @@ def test_select_path_thresholds():
 
 
 def test_status_strings():
-    for c in (0, -1, -2, -3, -4, 7):
+    for c in (0, -1, -2, -3, -4, -5, 7):
         assert mx.moe_status_string(c)
 
 
@@ -171,3 +171,25 @@ def test_next_row_entry_points_validate_on_the_host():
     assert L.moe_eplb_migrate(ctypes.byref(d), G[0], 0, *G[1:9], None) == -1
     assert L.moe_eplb_migrate(ctypes.byref(d), G[0], 384, P(0x1001), *G[2:9], None) == -1
     assert L.moe_eplb_migrate(ctypes.byref(_dims(H=100)), G[0], 384, *G[1:9], None) == -1
+
+
+def test_noalloc_entry_validates_on_the_host():
+    """moe_forward_noalloc refuses dims beyond its fixed scratch (and bad dims)
+    before it touches the GPU; the scratch size matches the header's."""
+    L = mx.lib()
+    P = ctypes.c_void_p
+    G = [P(a) for a in GOOD]
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == mx.NOALLOC_SCRATCH_BYTES
+    # the stated capacity at d_model 7168, d_ff 2048, top-6
+    assert mx.moe_workspace_bytes(_dims(T=1, T_max=587)) <= mx.NOALLOC_SCRATCH_BYTES
+    assert mx.moe_workspace_bytes(_dims(T=1, T_max=588)) > mx.NOALLOC_SCRATCH_BYTES
+    chosen = ctypes.c_int(-1)
+    call = lambda d: L.moe_forward_noalloc(ctypes.byref(d), 0, *G[:10], ctypes.byref(chosen), None)  # noqa: E731
+    assert call(_dims(T=1, T_max=588)) == -5
+    assert call(_dims(T=8192, T_max=8192)) == -5
+    assert call(_dims(k=17)) == -2
+    assert call(_dims(T=600)) == -1
+    assert chosen.value == -1  # nothing chosen, nothing launched
+    assert "scratch" in mx.moe_status_string(-5)
