@@ -83,11 +83,10 @@ def forward_token(wl, t: int) -> np.ndarray:
 
 
 def act_error_bound(x_rows: np.ndarray, w1, w1s, h: np.ndarray, F: int, rel: float) -> np.ndarray:
-    """Bound on |act_gpu - act| from an accumulation error of ``rel`` times the
-    sum of absolute products in each GEMM1 output (gate g, up u):
-    |d act| <= |silu'(g)| eg |u| + |silu(g)| eu + eg eu, silu' <= 1.1."""
+    """Bound on |act_gpu - act| (before the bf16 rounding) from an
+    accumulation error of ``rel`` times the sum of absolute products in each
+    GEMM1 output, carried through SwiGLU as in the a8w4 layer
+    (oracle.moe.swiglu_error_terms)."""
     W = fm.dequant_mxfp4(w1, w1s)
     e = rel * (np.abs(x_rows) @ np.abs(W).T)
-    g, u = h[:, :F], h[:, F:]
-    eg, eu = e[:, :F], e[:, F:]
-    return 1.1 * eg * np.abs(u) + np.abs(om.silu(g)) * eu + eg * eu
+    return sum(om.swiglu_error_terms(h, e, F).values())

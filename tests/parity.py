@@ -193,13 +193,12 @@ def check_out(out_gpu_bits, ref_f64, what="", bound=None):
     return norm, elem
 
 
-def y_error_bound(act_dq, w2, w2s, rel=2.0 ** -14):
-    """A bound on |y_gpu - y| for GEMM2 rows on the same act: the block-scaled
-    MFMA's in-instruction rounding, ``rel`` = 2^-14 of sum_k |act_k w_k| (the
-    ratio the GEMM1 tie-zone bound uses, 2.4x the largest observation), plus
-    a few f32 ulps of y."""
-    W = np.abs(fm.dequant_mxfp4(w2, w2s))
-    return rel * (np.abs(act_dq) @ W.T) + 2.0 ** -21 * np.abs(act_dq @ fm.dequant_mxfp4(w2, w2s).T)
+def y_error_bound(act_dq, w2, w2s):
+    """A bound on |y_gpu - y| for GEMM2 rows on the same act: the oracle's
+    bound for a chain of block-scaled MFMA instructions accumulating in
+    float32 (oracle.moe.gemm_error_bound, the bound the GEMM1 tie-zone check
+    carries through SwiGLU)."""
+    return om.gemm_error_bound(act_dq, fm.dequant_mxfp4(w2, w2s))
 
 
 def conditioned_bound(tokens, ref, yb, d, out_ref):
