@@ -303,6 +303,17 @@ def test_sweep_16384_tokens():
     assert res["chosen"] == "large_m"
 
 
+@pytest.mark.parametrize("T", [1, 8, 1024, 4096])
+def test_sweep_points_at_full_width(T):
+    """Sweep points at d_model 7168 / d_ff 2048: one and eight tokens (the
+    small-input path with few touched experts), 1024 tokens (the large-input
+    path still streaming weights: 16 rows per slot, two 16-row token tiles per
+    pass) and 4096 (the tiled kernels with half-filled 128-token blocks and a
+    partial last round of items)."""
+    res = _big_check(synth.make_sweep(T), n_slots=2, n_tokens=12)
+    assert res["chosen"] == ("small_m" if T <= 512 else "large_m")
+
+
 def test_prefill_ep8_rank_share_65536_tokens():
     """The EP-shaped prefill share the benchmark times (8 ranks x 8192 tokens
     routed into this GPU's 48 experts, ~1030 rows per slot: nine 128-token
