@@ -109,8 +109,8 @@ typedef struct {
   int32_t large_m_min;     /* 0 -> 1024 [sglang PR 47065, Modifications]    */
 } moe_dims_t;
 
-/* Optional device copies of intermediate results for parity checks; any
- * member may be NULL.  Shapes as in the layout table above.  Every path
+/* Optional device copies of intermediate results for parity checks, and
+ * timing hooks; any member may be NULL.  Shapes as in the layout table above.  Every path
  * writes topk_ids, topk_w, phys_ids, counts and offsets.  STAGED and
  * LARGE_M (bucketed rows) write row_of_pair, pair_of_row, xq, xs, aq, as;
  * SMALL_M writes instead the per-token activations xq_tok u8 [T, H] /
@@ -133,6 +133,12 @@ typedef struct {
   uint8_t* xs_tok;
   uint8_t* aq_pair;
   uint8_t* as_pair;
+  /* Timing hooks (HOST values: hipEvent_t handles created by the caller, any
+   * may be NULL): moe_forward records gemm1_events[0] / [1] on `stream` right
+   * before / after its GEMM1 launch and gemm2_events likewise around GEMM2,
+   * so that a caller can time those kernels inside the whole forward. */
+  void* gemm1_events[2];
+  void* gemm2_events[2];
 } moe_taps_t;
 
 /* Bytes of device workspace every call below needs for `dims` (sized by
@@ -176,6 +182,14 @@ int moe_route(const moe_dims_t* dims, const float* logits, int32_t* topk_ids, fl
 int moe_eplb_remap_record(const moe_dims_t* dims, const int32_t* topk_ids, const int32_t* rep_count,
                           const int32_t* rep_slots, int32_t* phys_ids, int32_t* load_hist,
                           void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* The replica a2 sends a token to (host utility, no device call): the index
+ * r in [0, rep_count) of rep_slots[e][r] for global token id `token_id` of an
+ * expert with `rep_count` replicas, r = fmix32(token_id) mod rep_count
+ * (MurmurHash3's 32-bit finaliser).  The kernels use the same rule; a
+ * rep_count outside [1, R_max] (a broken table) is clamped into that range
+ * there and here, so that no table read leaves the expert's row. */
+int32_t moe_replica_of(uint32_t token_id, int32_t rep_count, int32_t R_max);
 
 /* a3 + a4. Bucket this GPU's pairs by local slot and quantise + dispatch the
  * activations [sglang PR 47065, intro: "quant, dispatch"].

@@ -32,7 +32,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_select_path", "moe_status_string", "moe_p
            "moe_grouped_gemm2_combine", "moe_grouped_gemm1_swiglu_pairs", "moe_grouped_gemm2_combine_pairs",
            "moe_forward", "moe_eplb_rebalance", "moe_eplb_migrate",
            "moe_router_workspace_bytes", "moe_router_logits", "moe_forward_small_m",
-           "moe_a16w4_workspace_bytes", "moe_forward_a16w4", "moe_forward_noalloc")
+           "moe_a16w4_workspace_bytes", "moe_forward_a16w4", "moe_forward_noalloc", "moe_replica_of")
 
 
 class MoeError(RuntimeError):
@@ -62,6 +62,14 @@ class Taps(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_ids", "topk_w", "phys_ids", "counts", "offsets",
                                                 "row_of_pair", "pair_of_row", "xq", "xs", "aq", "as_",
                                                 "xq_tok", "xs_tok", "aq_pair", "as_pair")]
+    _fields_ += [("gemm1_events", ctypes.c_void_p * 2), ("gemm2_events", ctypes.c_void_p * 2)]
+
+
+def _event_handle(ev) -> int:
+    """The hipEvent_t behind a torch.cuda.Event (torch creates it at the first record)."""
+    if ev.cuda_event == 0:
+        ev.record()
+    return ev.cuda_event
 
 
 _lib_handle = None
@@ -110,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.moe_router_workspace_bytes.restype = ctypes.c_size_t
         L.moe_router_logits.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
         L.moe_router_logits.restype = I
+        L.moe_replica_of.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32]
+        L.moe_replica_of.restype = ctypes.c_int32
         L.moe_eplb_rebalance.argtypes = [I, I, I, I, P, P, P, P, P]
         L.moe_eplb_migrate.argtypes = [D, P, I, P, P, P, P, P, P, P, P, P]
         for n in ("moe_pack_weights", "moe_route", "moe_eplb_remap_record", "moe_quant_permute",
@@ -179,6 +189,10 @@ def moe_select_path(d: Dims) -> str:
 
 def moe_status_string(code: int) -> str:
     return lib().moe_status_string(int(code)).decode()
+
+
+def moe_replica_of(token_id: int, rep_count: int, R_max: int) -> int:
+    return int(lib().moe_replica_of(int(token_id) & 0xFFFFFFFF, int(rep_count), int(R_max)))
 
 
 def moe_packed_bytes(d: Dims, which: int) -> int:
@@ -296,9 +310,12 @@ def make_taps(d: Dims, device="cuda") -> Dict[str, torch.Tensor]:
 
 
 def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, out, ws, load_hist=None,
-                path: str = "auto", taps: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> str:
+                path: str = "auto", taps: Optional[Dict[str, torch.Tensor]] = None, stream=None,
+                gemm_events=None) -> str:
     """Run the whole layer on packed weights; returns the path taken
-    ("small_m", "staged", "large_m")."""
+    ("small_m", "staged", "large_m").  ``gemm_events`` (optional): four
+    torch.cuda.Event recorded around the GEMM1 and the GEMM2 launch
+    (begin1, end1, begin2, end2)."""
     TK, TMK = _sizes(d)
     tp = None
     if taps is not None:
@@ -308,6 +325,10 @@ def moe_forward(d: Dims, x, logits, pw1, pw1s, pw2, pw2s, rep_count, rep_slots, 
                     as_=(u8, TMK * (d.F // 128)), xq_tok=(u8, d.T * d.H), xs_tok=(u8, d.T * (d.H // 128)),
                     aq_pair=(u8, TK * d.F), as_pair=(u8, TK * (d.F // 128)))
         tp = Taps(**{n: _ptr(taps.get(n), n, *need[n]) for n in need})
+    if gemm_events is not None:
+        tp = tp if tp is not None else Taps()
+        h = [_event_handle(e) for e in gemm_events]
+        tp.gemm1_events[0], tp.gemm1_events[1], tp.gemm2_events[0], tp.gemm2_events[1] = h
     chosen = ctypes.c_int(-1)
     rc = lib().moe_forward(
         ctypes.byref(d), PATHS[path], _ptr(x, "x", _bf16(x), d.T * d.H), _ptr(logits, "logits", f32, d.T * d.E),

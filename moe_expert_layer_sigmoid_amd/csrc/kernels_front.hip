@@ -173,10 +173,9 @@ __global__ __launch_bounds__(256) void k_count(int T, int k, const int32_t* __re
     int p = -1;  // padding never matches a slot
     if (i < np) {
       if (do_remap) {
-        int e = ids[pr0 + i];
-        uint32_t h = fmix32(token_id_base + (uint32_t)(t0 + i / k));
-        int r = (int)(h % (uint32_t)rep_count[e]);
-        p = rep_slots[(size_t)e * R_max + r];
+        const int e = ids[pr0 + i];
+        const uint32_t h = fmix32(token_id_base + (uint32_t)(t0 + i / k));
+        p = rep_slots[(size_t)e * R_max + replica(h, rep_count[e], R_max)];
         phys[pr0 + i] = p;
       } else {
         p = phys[pr0 + i];
@@ -411,14 +410,48 @@ hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* p
 }
 
 // ---------------------------------------------------------------------------
+// a7, tokens with exactly one local pair: their output row is one term,
+// bf16(fma(w, y, 0)), which the bucketed GEMM2 kernels write themselves from
+// their accumulators (the combine then skips those tokens, and their f32 y
+// row is never written or read).  One thread per token: rtok[row] = t for the
+// row of such a token, -1 for the rows of tokens with two or more local
+// pairs; rw[row] = the pair's routing weight.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_single_rows(int T, int k, const int32_t* __restrict__ row_of_pair,
+                                                     const float* __restrict__ w, int32_t* __restrict__ rtok,
+                                                     float* __restrict__ rw) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int32_t* rp = row_of_pair + (size_t)t * k;
+  int n = 0;
+  for (int j = 0; j < k; ++j) n += rp[j] >= 0;
+  for (int j = 0; j < k; ++j) {
+    const int r = rp[j];
+    if (r >= 0) {
+      rtok[r] = n == 1 ? t : -1;
+      rw[r] = w[(size_t)t * k + j];
+    }
+  }
+}
+
+hipError_t launch_single_rows(int T, int k, const int32_t* row_of_pair, const float* w, int32_t* rtok, float* rw,
+                              hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  k_single_rows<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(T, k, row_of_pair, w, rtok, rw);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // a7 combine: one wavefront per (token, kCC 512-column chunks), 8 columns per
 // lane and chunk; out[t] = sum over local j ascending of w[t][j] *
 // y[row(t, j)] (f32 fma chain), rounded to bf16 (nearest even).  A row's
-// loads for all the wave's chunks are issued together.
+// loads for all the wave's chunks are issued together.  With skip_single,
+// tokens with exactly one local pair are left alone (GEMM2 wrote them).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const float* __restrict__ y,
                                                  const int32_t* __restrict__ row_of_pair,
-                                                 const float* __restrict__ w, uint16_t* __restrict__ out) {
+                                                 const float* __restrict__ w, uint16_t* __restrict__ out,
+                                                 int skip_single) {
   const int lane = threadIdx.x & 63;
   const int ng = (H + 512 * kCC - 1) / (512 * kCC);
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -432,12 +465,15 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
   }
   int rows[16];
   float ws[16];
+  int nloc = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     int r = __shfl(myrow, j);
     ws[j] = __shfl(myw, j);
     rows[j] = j < k ? r : -1;
+    nloc += rows[j] >= 0;
   }
+  if (skip_single && nloc == 1) return;  // wave-uniform: GEMM2 wrote this row
   float a[kCC][8];
 #pragma unroll
   for (int c = 0; c < kCC; ++c)
@@ -480,10 +516,10 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
 }
 
 hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* row_of_pair, const float* w,
-                          uint16_t* out, hipStream_t st) {
+                          uint16_t* out, bool skip_single, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const long waves = (long)T * ((H + 512 * kCC - 1) / (512 * kCC));
-  k_combine<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, y, row_of_pair, w, out);
+  k_combine<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, y, row_of_pair, w, out, skip_single ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -534,7 +570,7 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(
     if (tv && lane < k) {
       const size_t pr = (size_t)t * k + lane;
       const uint32_t h = fmix32(token_id_base + (uint32_t)t);
-      const int r = (int)(h % (uint32_t)s_rc[id]);
+      const int r = replica(h, s_rc[id], R_max);
       p = lds_tab ? s_rs[id * R_max + r] : rep_slots[(size_t)id * R_max + r];
       ids[pr] = id;
       w[pr] = wt;

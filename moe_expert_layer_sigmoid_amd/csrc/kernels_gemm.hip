@@ -99,14 +99,20 @@ __device__ __forceinline__ v4f mfma_ij(v4i a, v8i b, v4f c, int sa, int sb) {
 }
 
 // One wave's operands: packed weight tiles (A) and NT token tiles (B) that
-// share each weight load.
-template <int NT>
+// share each weight load.  UT: the tile offsets wt / wst are wave-uniform
+// (scalar registers) and the lane's own offset is wl / sl; otherwise wt / wst
+// hold the lane's full offsets.  (GEMM2 takes the uniform form, GEMM1 the
+// per-lane one: with these, each fits its 168-register budget without
+// spilling.)
+template <int NT, bool UT = false>
 struct SOps {
   rsrc_t w;                // packed data of the slot
   rsrc_t ws;               // packed scales of the slot
   rsrc_t x;                // the token rows
-  uint32_t wt[4];          // tile * data_tile + 16 * lane
-  uint32_t wst[4];         // tile * scale_tile + 8 * lane
+  uint32_t wl;             // UT: 16 * lane, the lane's bytes in a 1 KB weight load
+  uint32_t sl;             // UT: 8 * lane, the lane's bytes in a 512 B scale load
+  uint32_t wt[4];          // tile * data_tile (+ 16 * lane unless UT)
+  uint32_t wst[4];         // tile * scale_tile (+ 8 * lane unless UT)
   uint32_t xlo[NT];        // per token tile: token row * K + 16 g (past the buffer: zeros)
   uint32_t kx;             // K of the token rows (bytes)
   uint32_t lim;            // the token buffer's size: offsets from here read zeros
@@ -121,13 +127,18 @@ struct SStage {
 
 // Operands of K step st; `gofs` moves the weight tiles to another group of
 // the wave's tiles (a uniform byte offset).
-template <int WAUX, int NT>
-__device__ __forceinline__ void s_load(SStage<NT>& S, const SOps<NT>& O, int st, uint32_t gofs = 0) {
+template <int WAUX, int NT, bool UT>
+__device__ __forceinline__ void s_load(SStage<NT>& S, const SOps<NT, UT>& O, int st, uint32_t gofs = 0) {
   const uint32_t wo = (uint32_t)st * 2048 + gofs, xo = (uint32_t)st * 256;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    S.a[rt][0] = buf_load16_p<WAUX>(O.w, O.wt[rt], wo);
-    S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wt[rt] + 1024, wo);
+    if constexpr (UT) {
+      S.a[rt][0] = buf_load16_p<WAUX>(O.w, O.wl, O.wt[rt] + wo);
+      S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wl, O.wt[rt] + wo + 1024);
+    } else {
+      S.a[rt][0] = buf_load16_p<WAUX>(O.w, O.wt[rt], wo);
+      S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wt[rt] + 1024, wo);
+    }
   }
   // Steps past K (the packed weights pad K to a multiple of 1024) take zero
   // tokens, not the bytes after the row: those may belong to rows nothing
@@ -150,11 +161,12 @@ struct SScales {
   int lo[4], hi[4];  // steps 4q, 4q+1 (lo) and 4q+2, 4q+3 (hi) of each tile
 };
 
-template <int NT>
-__device__ __forceinline__ void s_load_scales(SScales& C, const SOps<NT>& O, int q, uint32_t gofs = 0) {
+template <int NT, bool UT>
+__device__ __forceinline__ void s_load_scales(SScales& C, const SOps<NT, UT>& O, int q, uint32_t gofs = 0) {
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const v2i v = buf_load8(O.ws, O.wst[rt], (uint32_t)q * 512 + gofs);
+    const v2i v = UT ? buf_load8(O.ws, O.sl, O.wst[rt] + (uint32_t)q * 512 + gofs)
+                     : buf_load8(O.ws, O.wst[rt], (uint32_t)q * 512 + gofs);
     C.lo[rt] = v.x;
     C.hi[rt] = v.y;
   }
@@ -189,8 +201,8 @@ __device__ __forceinline__ void s_mma(v4f (&acc)[4][NT], const SStage<NT>& S, co
 // no branches (its last loads re-read the final steps and are never used).
 // After a group's last step epi(g, acc) consumes its results and acc restarts
 // at zero.  WAUX: cache policy of the weight loads.
-template <int WAUX, int G, int NT, typename Epi>
-__device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT>& O, int S4, uint32_t gd, uint32_t sgd,
+template <int WAUX, int G, int NT, bool UT, typename Epi>
+__device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT, UT>& O, int S4, uint32_t gd, uint32_t sgd,
                                               Epi&& epi) {
   SStage<NT> s0, s1;
   SScales c0, c1;
@@ -241,8 +253,8 @@ __device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT>&
 }
 
 // One group: all S4 steps of NT token tiles, results left in acc.
-template <int WAUX, int NT>
-__device__ __forceinline__ void stream_tile(v4f (&acc)[4][NT], const SOps<NT>& O, int S4) {
+template <int WAUX, int NT, bool UT>
+__device__ __forceinline__ void stream_tile(v4f (&acc)[4][NT], const SOps<NT, UT>& O, int S4) {
   v4f res[4][NT];
   stream_groups<WAUX, 1>(acc, O, S4, 0u, 0u, [&](int, const v4f(&a)[4][NT]) {
 #pragma unroll
@@ -270,10 +282,12 @@ constexpr int kPairRows = kPairMaxT;  // rows of one slot on the pair-indexed pa
 template <typename Src>
 __device__ __forceinline__ void stage_token_scales(uint8_t* s_xs, const uint8_t* xs, int nrow, int nb, int S4,
                                                    int rows, Src src) {
+  // 16 threads per row: no division by the run-time pitch
   const int pitch = 2 * S4;
-  for (int i = threadIdx.x; i < rows * pitch; i += blockDim.x) {
-    const int r = i / pitch, c = i - r * pitch;
-    s_xs[i] = (r < nrow && c < nb) ? xs[(size_t)src(r) * nb + c] : (uint8_t)0;
+  for (int r = (int)(threadIdx.x >> 4); r < rows; r += (int)(blockDim.x >> 4)) {
+    const bool ok = r < nrow;
+    const uint8_t* row = xs + (ok ? (size_t)src(r) * nb : 0);
+    for (int c = threadIdx.x & 15; c < pitch; c += 16) s_xs[r * pitch + c] = (ok && c < nb) ? row[c] : (uint8_t)0;
   }
 }
 
@@ -326,8 +340,8 @@ __device__ __forceinline__ SlotRows<PAIRS> listed_rows(const int32_t* counts, co
 // slot): a buffer over the input rows and this lane's byte offsets.  Lanes
 // past the rows read zeros (an offset past the buffer); their results are
 // never stored.
-template <bool PAIRS, int NT>
-__device__ __forceinline__ void token_operand(SOps<NT>& O, const uint8_t* x, const SlotRows<PAIRS>& R, int tt0,
+template <bool PAIRS, int NT, bool UT>
+__device__ __forceinline__ void token_operand(SOps<NT, UT>& O, const uint8_t* x, const SlotRows<PAIRS>& R, int tt0,
                                               int nrow, int nsrc, int K, int l16, int g) {
   const uint32_t lim = PAIRS ? (uint32_t)nsrc * (uint32_t)K : (uint32_t)nrow * (uint32_t)K;
   O.x = PAIRS ? make_rsrc(x, lim) : make_rsrc(x + (size_t)(R.row0 + tt0) * K, lim);
@@ -397,7 +411,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm1_stream(
     __syncthreads();  // previous pass's readers of s_xs / s_amax are done
     stage_token_scales(s_xs, xs, nrow, nb, S4, kRows, [&](int r) { return R.src(tt0 + r); });
     __syncthreads();
-    token_operand<PAIRS, NT>(O, xq, R, tt0, nrow, nsrc, H, l16, g);
+    token_operand<PAIRS, NT, false>(O, xq, R, tt0, nrow, nsrc, H, l16, g);
 #pragma unroll
     for (int t = 0; t < NT; ++t) O.sxs[t] = s_xs + (t * 16 + l16) * 2 * S4;
     v4f acc[4][NT];
@@ -457,7 +471,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ phys, int np, int p0, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ plist, int stride, int nsrc, const uint8_t* __restrict__ pw2,
-    const uint8_t* __restrict__ pw2s, float* __restrict__ y, int H, int F) {
+    const uint8_t* __restrict__ pw2s, float* __restrict__ y, int H, int F, SingleRows sr) {
   constexpr int kRows = 16 * NT;  // token rows per pass
   __shared__ __align__(16) uint8_t s_xs[kRows * 2 * kMaxSteps];
   __shared__ int s_list[PAIRS ? kPairRows : 1];
@@ -476,14 +490,16 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
   const PackGeom G = pack_geom((uint32_t)H, (uint32_t)F);
   const int S4 = (int)G.steps;
   const int nb = F / kActBlock;
-  SOps<NT> O;
+  SOps<NT, true> O;
   O.w = make_rsrc(pw2 + (size_t)s * G.data_slot, (uint32_t)G.data_slot);
   O.ws = make_rsrc(pw2s + (size_t)s * G.scale_slot, (uint32_t)G.scale_slot);
+  O.wl = 16u * lane;
+  O.sl = 8u * lane;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const uint32_t tile = live ? (uint32_t)(h0 / 16 + rt) : 0u;
-    O.wt[rt] = tile * (uint32_t)G.data_tile + 16u * lane;
-    O.wst[rt] = tile * (uint32_t)G.scale_tile + 8u * lane;
+    O.wt[rt] = tile * (uint32_t)G.data_tile;
+    O.wst[rt] = tile * (uint32_t)G.scale_tile;
   }
   const uint32_t gd = 4u * (uint32_t)G.data_tile, sgd = 4u * (uint32_t)G.scale_tile;
   for (int tt0 = 0; tt0 < n; tt0 += kRows) {
@@ -492,13 +508,31 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
     stage_token_scales(s_xs, as_, nrow, nb, S4, kRows, [&](int r) { return R.src(tt0 + r); });
     __syncthreads();
     if (!live) continue;
-    token_operand<PAIRS, NT>(O, aq, R, tt0, nrow, nsrc, F, l16, g);
-    float* yr[NT];
+    token_operand<PAIRS, NT, true>(O, aq, R, tt0, nrow, nsrc, F, l16, g);
+    // y through a buffer: pair rows index all of y (T k H 4 bytes < 2^31 for
+    // T <= 1024), bucketed rows the pass's own rows; lanes past the rows
+    // store beyond the buffer, which drops them
+    const uint32_t ylim = (PAIRS ? (uint32_t)nsrc : (uint32_t)nrow) * (uint32_t)H * 4u;
+    const rsrc_t Yr = PAIRS ? make_rsrc(y, ylim) : make_rsrc(y + (size_t)(R.row0 + tt0) * H, ylim);
+    // bucketed rows of tokens with exactly one local pair: the output row
+    // bf16(fma(w, y, 0)) instead of y (sr.rtok null: none)
+    // (one offset per lane: into y, or into out when ow >= 0, the routing
+    // weight of a single-pair row; routing weights are never negative)
+    const rsrc_t Or = make_rsrc(sr.out, sr.rtok ? sr.out_bytes : 0u);
+    uint32_t off[NT];
+    float ow[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = t * 16 + l16;
       O.sxs[t] = s_xs + r * 2 * S4;
-      yr[t] = r < nrow ? y + (size_t)R.dst(tt0 + r) * H + h0 + 4 * g : nullptr;
+      const uint32_t row = PAIRS ? (uint32_t)R.dst(tt0 + (r < nrow ? r : 0)) : (uint32_t)r;
+      int tok = -1;
+      if constexpr (!PAIRS) {
+        if (sr.rtok != nullptr && r < nrow) tok = sr.rtok[R.row0 + tt0 + r];
+      }
+      ow[t] = tok >= 0 ? sr.rw[R.row0 + tt0 + r] : -1.0f;
+      off[t] = tok >= 0 ? ((uint32_t)tok * (uint32_t)H + (uint32_t)(h0 + 4 * g)) * 2u
+                        : (r < nrow ? (row * (uint32_t)H + (uint32_t)(h0 + 4 * g)) * 4u : ylim);
     }
     v4f acc[4][NT];
 #pragma unroll
@@ -507,13 +541,27 @@ __global__ __launch_bounds__(256, NT == 1 ? 3 : 2) void k_gemm2_stream(
       for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0.f, 0.f, 0.f, 0.f};
     stream_groups<kWeightAux, 1>(acc, O, S4, gd, sgd, [&](int grp, const v4f(&a)[4][NT]) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (yr[t] == nullptr) continue;
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          *reinterpret_cast<float4*>(yr[t] + 64 * grp + 16 * rt) =
-              make_float4(a[rt][t][0], a[rt][t][1], a[rt][t][2], a[rt][t][3]);
-      }
+        for (int rt = 0; rt < 4; ++rt) {
+          // column offsets go into the lane offset, soffset stays 0: the
+          // compiler guards the store data of a 16-byte buffer store against
+          // the next VALU write only when soffset is not a register, and
+          // gfx950 needs that guard (a register soffset here let the next
+          // instruction's write reach the stored data)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, a[rt][t]), Yr,
+                                                 (ow[t] < 0.0f ? off[t] : ylim) + (uint32_t)(64 * grp + 16 * rt) * 4u,
+                                                 0, 0);
+          if constexpr (!PAIRS) {
+            const v4f& v = a[rt][t];
+            const v2i o = {(int)((uint32_t)f32_to_bf16(fmaf(ow[t], v[0], 0.0f)) |
+                                 ((uint32_t)f32_to_bf16(fmaf(ow[t], v[1], 0.0f)) << 16)),
+                           (int)((uint32_t)f32_to_bf16(fmaf(ow[t], v[2], 0.0f)) |
+                                 ((uint32_t)f32_to_bf16(fmaf(ow[t], v[3], 0.0f)) << 16))};
+            __builtin_amdgcn_raw_buffer_store_b64(
+                o, Or, (ow[t] >= 0.0f ? off[t] : sr.out_bytes) + (uint32_t)(64 * grp + 16 * rt) * 2u, 0, 0);
+          }
+        }
     });
   }
 }
@@ -534,19 +582,22 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
 template <bool PAIRS>
 static void gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const int32_t* phys, int np,
                          int p0, const int32_t* counts, const int32_t* plist, int stride, int nsrc, const uint8_t* pw2,
-                         const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
+                         const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, SingleRows sr,
+                         hipStream_t st) {
   const unsigned grid = (unsigned)(P_local * ((H + kG2Rows - 1) / kG2Rows));
   if (nt >= 2)
     k_gemm2_stream<PAIRS, 2><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, counts, plist, stride, nsrc, pw2,
-                                                    pw2s, y, H, F);
+                                                    pw2s, y, H, F, sr);
   else
     k_gemm2_stream<PAIRS, 1><<<grid, 256, 0, st>>>(aq, as, offsets, phys, np, p0, counts, plist, stride, nsrc, pw2,
-                                                    pw2s, y, H, F);
+                                                    pw2s, y, H, F, sr);
 }
 
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
-  gemm2_stream<false>(aq, as, offsets, nullptr, 0, 0, nullptr, nullptr, 0, 0, pw2, pw2s, y, H, F, P_local, nt, st);
+                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, SingleRows sr,
+                               hipStream_t st) {
+  gemm2_stream<false>(aq, as, offsets, nullptr, 0, 0, nullptr, nullptr, 0, 0, pw2, pw2s, y, H, F, P_local, nt, sr,
+                      st);
   return hipGetLastError();
 }
 
@@ -567,7 +618,7 @@ hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_
                               const int32_t* counts, const int32_t* plist, int stride, const uint8_t* pw2,
                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st) {
   gemm2_stream<true>(aq, as, nullptr, phys, T * k, p0, counts, plist, stride, T * k, pw2, pw2s, y, H, F, P_local, nt,
-                     st);
+                     SingleRows{nullptr, nullptr, nullptr, 0u}, st);
   return hipGetLastError();
 }
 

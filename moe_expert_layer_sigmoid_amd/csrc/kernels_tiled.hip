@@ -31,6 +31,8 @@
 //    runs at 63-67 % of the MFMA rate; GEMM2's items are short, K = 2048,
 //    and its y-store epilogue, all CUs writing at once, is a quarter of each.)
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "moe_device.hpp"
@@ -72,6 +74,11 @@ __device__ __forceinline__ v4i lds_read16_at(uint32_t a) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFS));
   return v;
 }
+// ds_write_b64 of `v` at LDS address `a` + OFS (an immediate)
+template <int OFS>
+__device__ __forceinline__ void lds_write8_at(uint32_t a, v2i v) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(a), "v"(v), "i"(OFS) : "memory");
+}
 __device__ __forceinline__ v2i lds_read8(const void* p) {
   v2i v;
   asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(lds_addr(p)));
@@ -108,11 +115,17 @@ constexpr int kXI = kStage / 1024 / kWaves;  // token DMA instructions per wave 
 constexpr int kWI = 4;                       // weight DMA instructions per wave per stage
 // A stage's DMA is waited for at the start of the stage two later, with one
 // more stage of DMA issued after it; an epilogue's stores follow the DMA of
-// the next item's first two stages (GEMM1: 3 per token tile, GEMM2: 4).
+// the next item's first two stages (GEMM1: 3 per token tile; GEMM2: 4 of y
+// and 2 of bf16 output rows per token tile).
 constexpr int kVmWait = kXI + kWI;
 template <bool G1>
-constexpr int kEpiStores = G1 ? 3 * 8 : 4 * 8;
+constexpr int kEpiStores = G1 ? 3 * 8 : 6 * 8;
+// GEMM2's bf16 output rows pass through LDS on their way out: per wave, 16
+// rows of 64 bf16 values with a padded pitch (in the ring slot that no DMA
+// targets at the item's end).
+constexpr int kOutPitch = 144;
 static_assert(kVmWait + kEpiStores<false> <= 63, "vmcnt range");
+static_assert(kWaves * 16 * kOutPitch <= kStage + kWStage, "output rows fit one ring slot");
 constexpr size_t kStaticLds = (size_t)kRing * (kStage + kWStage) + kTM * kMaxStages;
 // dynamic LDS: the requant amax, the item prefix and the bucket offsets
 static size_t tiled_lds(int P_local) { return kWaves * kTM * sizeof(float) + 2 * (size_t)(P_local + 1) * sizeof(int); }
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
                                                         const int32_t* __restrict__ offsets, int P_local,
                                                         const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws,
                                                         uint8_t* __restrict__ aq, uint8_t* __restrict__ as_,
-                                                        float* __restrict__ y, int H, int F) {
+                                                        float* __restrict__ y, int H, int F, SingleRows sr) {
   __shared__ __align__(16) uint8_t g0s[kStage + kWStage], g1s[kStage + kWStage], g2s[kStage + kWStage];
   __shared__ __align__(16) uint8_t s_xs[kTM * kMaxStages];  // [stage][16][8] token scales
   extern __shared__ __align__(16) uint8_t lds[];
@@ -134,6 +147,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
   const int ngrp = (int)Gm.steps / 4;  // scale words of 8 stages
   float* s_amax = reinterpret_cast<float*>(lds);               // [8 waves][kTM]
   int* s_pre = reinterpret_cast<int*>(s_amax + kWaves * kTM);  // [P_local + 1] items before slot
+  // GEMM2: the current item's rows of single-pair tokens (the GEMM1 amax area):
+  // s_rinf[r] = token of row r (or -1), s_rinf[kTM + r] = its routing weight
+  int* s_rinf = reinterpret_cast<int*>(lds);
   int* s_off = s_pre + P_local + 1;                            // [P_local + 1] bucket offsets
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,6 +289,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
     }
   };
 
+  // GEMM2: row info of an item's rows (threads 0..127: token or -1,
+  // 128..255: routing weight), fetched early and stored after the barrier
+  // that ends the previous item
+  const bool fuse = !G1 && sr.rtok != nullptr;
+  auto rinf_fetch = [&](const TItem it) -> int {
+    const int r = tid & (kTM - 1);
+    int v = -1;
+    if (fuse && tid < 2 * kTM && it.live && r < it.nvalid)
+      v = tid < kTM ? __hip_atomic_load(sr.rtok + it.r0 + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                    : __hip_atomic_load(reinterpret_cast<const int*>(sr.rw) + it.r0 + r, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_WORKGROUP);
+    return v;
+  };
+  auto rinf_store = [&](int v) {
+    if (!G1 && tid < 2 * kTM) s_rinf[tid] = v;
+  };
+
   const int o_lo = (g ^ sw) * 16, o_hi = ((g + 4) ^ sw) * 16;
   v2i scc[4], scn[4];  // weight scales: the current group, the next one
   v4f acc[4][8];
@@ -338,6 +371,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
     uint32_t v[kXsPer];
     xs_fetch(cur, v);
     xs_store(cur, v);
+    rinf_store(rinf_fetch(cur));
   }
   load_scales(cur, 0, scn);
   __syncthreads();
@@ -394,22 +428,58 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
     }
     uint32_t xsn[kXsPer];
     xs_fetch(nxt, xsn);
+    const int rinfn = rinf_fetch(nxt);
     stage(nst4 - 4);
     stage(nst4 - 3);
     stage(nst4 - 2);
     stage(nst4 - 1);
 
     if (!G1) {
-      // ---- GEMM2 epilogue: y rows through a buffer sized to the item's rows
-      // (zero-sized for waves past H); the next stages' waits do not drain it
+      // ---- GEMM2 epilogue.  Rows of tokens with two or more local pairs (all
+      // rows without the fusion): f32 y through a buffer sized to the item's
+      // rows (zero-sized for waves past H).  Rows of tokens with exactly one
+      // local pair: bf16(fma(w, y, 0)) into their output row, regrouped
+      // through LDS so that each lane stores 16 consecutive values.  Every
+      // store is issued by every lane (an unused one lands past its buffer),
+      // so the count the next stages' waits rely on is exact; the next
+      // stages' waits do not drain them.
       const int h0 = cur.wb * 2 * kCols + wave * 64;
-      const rsrc_t Yr = make_rsrc(y + (size_t)cur.r0 * H, cur.wlive ? (uint32_t)cur.nvalid * (uint32_t)H * 4u : 0u);
+      const uint32_t ylim = cur.wlive ? (uint32_t)cur.nvalid * (uint32_t)H * 4u : 0u;
+      const rsrc_t Yr = make_rsrc(y + (size_t)cur.r0 * H, ylim);
+      const uint32_t olim = (fuse && cur.wlive) ? sr.out_bytes : 0u;
+      const rsrc_t Or = make_rsrc(sr.out, olim);
+      bare_barrier();  // every wave is done reading the last stage's ring slot
+      const uint8_t* tr = ring(slot == 0 ? kRing - 1 : slot - 1) + wave * (16 * kOutPitch);
+      const uint32_t trw = lds_addr(tr + l16 * kOutPitch + 8 * g);   // row l16, values 16 i + 4 g ..
+      const uint32_t trr = lds_addr(tr + l16 * kOutPitch + 32 * g);  // row l16, values 16 g .. 16 g + 15
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const uint32_t yo = ((uint32_t)(tt * 16 + l16) * (uint32_t)H + (uint32_t)(cur.wlive ? h0 + 4 * g : 0)) * 4u;
+        const int row = tt * 16 + l16;
+        const int tok = s_rinf[row];  // -1: y (no fusion, several local pairs, or past the rows)
+        const float wgt = __int_as_float(s_rinf[kTM + row]);
+        const uint32_t yo =
+            tok < 0 ? ((uint32_t)row * (uint32_t)H + (uint32_t)(cur.wlive ? h0 + 4 * g : 0)) * 4u : ylim;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][tt]), Yr, yo + 64u * i, 0, 0);
+        v2i o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i].x = (int)((uint32_t)f32_to_bf16(fmaf(wgt, acc[i][tt][0], 0.0f)) |
+                         ((uint32_t)f32_to_bf16(fmaf(wgt, acc[i][tt][1], 0.0f)) << 16));
+          o[i].y = (int)((uint32_t)f32_to_bf16(fmaf(wgt, acc[i][tt][2], 0.0f)) |
+                         ((uint32_t)f32_to_bf16(fmaf(wgt, acc[i][tt][3], 0.0f)) << 16));
+        }
+        lds_write8_at<0>(trw, o[0]);
+        lds_write8_at<32>(trw, o[1]);
+        lds_write8_at<64>(trw, o[2]);
+        lds_write8_at<96>(trw, o[3]);
+        MOE_LGKM_WAIT(0);
+        const v4i r0 = lds_read16_at<0>(trr), r1 = lds_read16_at<16>(trr);
+        MOE_LGKM_WAIT(0);
+        const uint32_t oo = tok >= 0 ? ((uint32_t)tok * (uint32_t)H + (uint32_t)(h0 + 16 * g)) * 2u : olim;
+        __builtin_amdgcn_raw_buffer_store_b128(r0, Or, oo, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(r1, Or, oo + 16u, 0, 0);
       }
     } else {
       // ---- epilogue: SwiGLU in place (acc[0..1] become act of the gate
@@ -459,21 +529,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
       }
     }
     after_epi = true;
-    bare_barrier();  // every wave is done with this item's token scales and amax
+    bare_barrier();  // every wave is done with this item's token scales, amax and row info
     xs_store(nxt, xsn);
+    rinf_store(rinfn);
     MOE_LGKM_WAIT(0);
     cur = nxt;
   }
 }
 
+// Compute units of the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_num_cus[kMaxDevices];
+
 static int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int n = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
   }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev >= 0 && dev < kMaxDevices) g_num_cus[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -482,15 +559,19 @@ bool tiled_fits(int H, int F, int P_local) {
 }
 
 // Dynamic LDS above the default limit is opted into per kernel and device,
-// once per size.
-static hipError_t grant_lds(const void* fn, size_t lds, size_t (&granted)[64]) {
+// once per size (the largest granted so far), under a lock: callers on other
+// threads may launch on the same device.
+static std::mutex g_lds_mu;
+
+static hipError_t grant_lds(const void* fn, size_t lds, size_t (&granted)[kMaxDevices]) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || lds > granted[dev]) {
+  std::lock_guard<std::mutex> lock(g_lds_mu);
+  if (dev < 0 || dev >= kMaxDevices || lds > granted[dev]) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) granted[dev] = lds;
+    if (dev >= 0 && dev < kMaxDevices) granted[dev] = lds;
   }
   return hipSuccess;
 }
@@ -499,21 +580,23 @@ hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_
                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
                               hipStream_t st) {
   const size_t lds = tiled_lds(P_local);
-  static size_t granted[64] = {};
+  static size_t granted[kMaxDevices] = {};
   hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_tiled<true>), lds, granted);
   if (e != hipSuccess) return e;
-  k_tiled<true><<<num_cus() / 8 * 8, kWaves * 64, lds, st>>>(xq, xs, offsets, P_local, pw1, pw1s, aq, as, nullptr, H, F);
+  k_tiled<true><<<num_cus() / 8 * 8, kWaves * 64, lds, st>>>(xq, xs, offsets, P_local, pw1, pw1s, aq, as, nullptr, H, F,
+                                                          SingleRows{nullptr, nullptr, nullptr, 0u});
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                              const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st) {
+                              const uint8_t* pw2s, float* y, int H, int F, int P_local, SingleRows sr,
+                              hipStream_t st) {
   const size_t lds = tiled_lds(P_local);
-  static size_t granted[64] = {};
+  static size_t granted[kMaxDevices] = {};
   hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_tiled<false>), lds, granted);
   if (e != hipSuccess) return e;
   k_tiled<false><<<num_cus() / 8 * 8, kWaves * 64, lds, st>>>(aq, as, offsets, P_local, pw2, pw2s, nullptr, nullptr, y,
-                                                           H, F);
+                                                           H, F, sr);
   return hipGetLastError();
 }
 

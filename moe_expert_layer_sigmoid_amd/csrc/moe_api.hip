@@ -20,7 +20,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, phys, rank, partial, base, counts, offsets, rop, por, xq, xs, aq, as, y, plist, total;
+  size_t ids, w, phys, rank, partial, base, counts, offsets, rop, por, xq, xs, aq, as, y, plist, rtok, rw, total;
 };
 
 // One workspace serves every call; regions are sized by T_max.
@@ -53,6 +53,9 @@ Layout layout_of(const moe_dims_t* d) {
   L.y = take(TK * d->H * 4);
   // per-slot pair lists of the pair-indexed GEMMs (GEMM1 -> GEMM2)
   L.plist = take((size_t)d->P_local * pair_list_stride(d->T_max, d->k) * 4);
+  // bucketed rows of single-pair tokens (GEMM2 writes their output rows)
+  L.rtok = take(TK * 4);
+  L.rw = take(TK * 4);
   L.total = off;
   return L;
 }
@@ -124,9 +127,31 @@ hipError_t gemm1(moe_path_t p, const uint8_t* xq, const uint8_t* xs, const int32
   return launch_gemm1_stream(xq, xs, offsets, pw1, pw1s, aq, as, d->H, d->F, d->P_local, stream_tiles(d), st);
 }
 hipError_t gemm2(moe_path_t p, const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                 const uint8_t* pw2s, float* y, const moe_dims_t* d, hipStream_t st) {
-  if (tiled_gemms(p, d)) return launch_gemm2_tiled(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st);
-  return launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, stream_tiles(d), st);
+                 const uint8_t* pw2s, float* y, SingleRows sr, const moe_dims_t* d, hipStream_t st) {
+  if (tiled_gemms(p, d)) return launch_gemm2_tiled(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, sr, st);
+  return launch_gemm2_stream(aq, as, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, stream_tiles(d), sr, st);
+}
+// GEMM2 + combine on bucketed rows.  Tokens with exactly one local pair get
+// their output row from GEMM2 itself (bf16(fma(w, y, 0)), the combine's
+// arithmetic for one term) and the combine skips them, whenever the output's
+// byte offsets fit the kernels' 32-bit buffer offsets (T H 2 < 2^32).
+hipError_t gemm2_combine(moe_path_t p, const uint8_t* aq, const uint8_t* as, const int32_t* offsets,
+                         const uint8_t* pw2, const uint8_t* pw2s, const int32_t* rop, const float* w, uint16_t* out,
+                         void* ws, const moe_dims_t* d, hipStream_t st) {
+  const Layout L = layout_of(d);
+  float* y = at<float>(ws, L.y);
+  const bool fuse = (uint64_t)d->T * (uint64_t)d->H * 2u < (1ull << 32);
+  SingleRows sr{nullptr, nullptr, nullptr, 0u};
+  if (fuse) {
+    int32_t* rtok = at<int32_t>(ws, L.rtok);
+    float* rw = at<float>(ws, L.rw);
+    hipError_t e = launch_single_rows(d->T, d->k, rop, w, rtok, rw, st);
+    if (e != hipSuccess) return e;
+    sr = SingleRows{rtok, rw, out, (uint32_t)((uint64_t)d->T * d->H * 2u)};
+  }
+  hipError_t e = gemm2(p, aq, as, offsets, pw2, pw2s, y, sr, d, st);
+  if (e != hipSuccess) return e;
+  return launch_combine(d->T, d->H, d->k, y, rop, w, out, fuse, st);
 }
 // The component GEMM calls pick by token count like MOE_PATH_AUTO.
 moe_path_t gemm_path(const moe_dims_t* d) {
@@ -174,6 +199,10 @@ int moe_pack_weights(const moe_dims_t* d, const uint8_t* w1, const uint8_t* w1s,
   MOE_TRY(launch_pack(w1, w1s, pw1, pw1s, d->P_local, 2 * d->F, d->H, st));
   MOE_TRY(launch_pack(w2, w2s, pw2, pw2s, d->P_local, d->H, d->F, st));
   return MOE_OK;
+}
+
+int32_t moe_replica_of(uint32_t token_id, int32_t rep_count, int32_t R_max) {
+  return replica(fmix32(token_id), rep_count, R_max < 1 ? 1 : R_max);
 }
 
 const char* moe_status_string(int s) {
@@ -262,10 +291,7 @@ int moe_grouped_gemm2_combine(const moe_dims_t* d, const uint8_t* aq, const uint
   if ((rc = check_ws(d, ws, ws_bytes))) return rc;
   if (d->T == 0) return MOE_OK;
   hipStream_t st = (hipStream_t)stream;
-  Layout L = layout_of(d);
-  float* y = at<float>(ws, L.y);
-  MOE_TRY(gemm2(gemm_path(d), aq, as, offsets, pw2, pw2s, y, d, st));
-  MOE_TRY(launch_combine(d->T, d->H, d->k, y, row_of_pair, topk_w, out, st));
+  MOE_TRY(gemm2_combine(gemm_path(d), aq, as, offsets, pw2, pw2s, row_of_pair, topk_w, out, ws, d, st));
   return MOE_OK;
 }
 
@@ -357,6 +383,7 @@ int forward_impl(const moe_dims_t* d, moe_path_t path, const int32_t* t_dev, con
   int32_t* partial = at<int32_t>(ws, L.partial);
   int32_t* base = at<int32_t>(ws, L.base);
   float* y = at<float>(ws, L.y);
+  auto mark = [&](void* ev) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev), st) : hipSuccess; };
 
   if (p == MOE_PATH_SMALL_M) {
     // pair-indexed: per-token activations in the xq/xs regions, pair rows in aq/as/y
@@ -369,10 +396,14 @@ int forward_impl(const moe_dims_t* d, moe_path_t path, const int32_t* t_dev, con
     const int nt = stream_tiles(d);
     int32_t* plist = at<int32_t>(ws, L.plist);
     const int stride = pair_list_stride(d->T_max, d->k);
+    MOE_TRY(mark(tp.gemm1_events[0]));
     MOE_TRY(launch_gemm1_pairs(xq_tok, xs_tok, phys, d->T, d->k, d->p0, pw1, pw1s, aq_p, as_p, counts, plist, stride,
                                d->H, d->F, d->P_local, nt, st));
+    MOE_TRY(mark(tp.gemm1_events[1]));
+    MOE_TRY(mark(tp.gemm2_events[0]));
     MOE_TRY(launch_gemm2_pairs(aq_p, as_p, phys, d->T, d->k, d->p0, counts, plist, stride, pw2, pw2s, y, d->H, d->F,
                                d->P_local, nt, st));
+    MOE_TRY(mark(tp.gemm2_events[1]));
     MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys, d->p0, d->P_local, w, out, partial,
                                  (d->T + kFrontTokens - 1) / kFrontTokens, d->P_total, load_hist, counts, offsets,
                                  st));
@@ -384,9 +415,21 @@ int forward_impl(const moe_dims_t* d, moe_path_t path, const int32_t* t_dev, con
                        d->p0, d->P_local, partial, rank, st));
   MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, counts, offsets, base, load_hist, st));
   MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys, d->p0, d->P_local, base, rank, xq, xs, rop, por, st));
+  MOE_TRY(mark(tp.gemm1_events[0]));
   MOE_TRY(gemm1(p, xq, xs, offsets, pw1, pw1s, aq, as, d, st));
-  MOE_TRY(gemm2(p, aq, as, offsets, pw2, pw2s, y, d, st));
-  MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, st));
+  MOE_TRY(mark(tp.gemm1_events[1]));
+  const bool fuse = (uint64_t)d->T * (uint64_t)d->H * 2u < (1ull << 32);
+  SingleRows sr{nullptr, nullptr, nullptr, 0u};
+  if (fuse) {
+    int32_t* rtok = at<int32_t>(ws, L.rtok);
+    float* rw = at<float>(ws, L.rw);
+    MOE_TRY(launch_single_rows(d->T, d->k, rop, w, rtok, rw, st));
+    sr = SingleRows{rtok, rw, out, (uint32_t)((uint64_t)d->T * d->H * 2u)};
+  }
+  MOE_TRY(mark(tp.gemm2_events[0]));
+  MOE_TRY(gemm2(p, aq, as, offsets, pw2, pw2s, y, sr, d, st));
+  MOE_TRY(mark(tp.gemm2_events[1]));
+  MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, fuse, st));
   return MOE_OK;
 }
 
@@ -500,7 +543,7 @@ int moe_forward_a16w4(const moe_dims_t* d, const uint16_t* x, const float* logit
                        at<uint8_t>(ws, L.xs), rop, por, st));
   MOE_TRY(launch_gemm1_a16(x, d->T, offsets, por, d->k, pw1, pw1s, act, d->H, d->F, d->P_local, st));
   MOE_TRY(launch_gemm2_a16(act, d->T_max * d->k, offsets, pw2, pw2s, y, d->H, d->F, d->P_local, st));
-  MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, st));
+  MOE_TRY(launch_combine(d->T, d->H, d->k, y, rop, w, out, false, st));
   return MOE_OK;
 }
 

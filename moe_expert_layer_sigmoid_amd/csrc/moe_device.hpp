@@ -21,13 +21,21 @@ constexpr int kFmtFp4 = 4;  // e2m1
 
 // MurmurHash3's 32-bit finaliser (Appleby, public domain): the replica hash
 // of the EPLB remap.
-__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+__host__ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   h ^= h >> 16;
   h *= 0x85ebca6bu;
   h ^= h >> 13;
   h *= 0xc2b2ae35u;
   h ^= h >> 16;
   return h;
+}
+
+// Replica index of a token hash for an expert with `count` replicas: h mod
+// count.  A count outside [1, R_max] breaks the caller's contract; it is
+// clamped so that the replica-table read stays inside the expert's row.
+__host__ __device__ __forceinline__ int replica(uint32_t h, int count, int R_max) {
+  const int c = count < 1 ? 1 : (count > R_max ? R_max : count);
+  return (int)(h % (uint32_t)c);
 }
 
 // Smallest integer e with amax <= 448 * 2^e (0 when amax == 0), clamped to

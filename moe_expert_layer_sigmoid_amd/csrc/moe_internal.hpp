@@ -28,8 +28,22 @@ hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* p
                         const int32_t* base, const int32_t* rank, uint8_t* xq, uint8_t* xs,
                         int32_t* row_of_pair, int32_t* pair_of_row, hipStream_t st);
 
+// skip_single: leave tokens with exactly one local pair alone (the bucketed
+// GEMM2 kernels wrote their rows, given launch_single_rows's row map).
 hipError_t launch_combine(int T, int H, int k, const float* y, const int32_t* row_of_pair, const float* w,
-                          uint16_t* out, hipStream_t st);
+                          uint16_t* out, bool skip_single, hipStream_t st);
+// Row map of tokens with exactly one local pair, for GEMM2 to write their
+// output rows: rtok [rows] = token (or -1: two or more local pairs), rw
+// [rows] = routing weight.
+hipError_t launch_single_rows(int T, int k, const int32_t* row_of_pair, const float* w, int32_t* rtok, float* rw,
+                              hipStream_t st);
+// The output rows GEMM2 writes for single-pair tokens (nullable rtok: none).
+struct SingleRows {
+  const int32_t* rtok;
+  const float* rw;
+  uint16_t* out;
+  uint32_t out_bytes;  // T H 2 (< 2^32)
+};
 
 // Small-M path (pair-indexed rows).  Front: routing, remap, per-16-token
 // chunk counts partial[ceil(T/16), P_total], and every token quantised into
@@ -58,7 +72,8 @@ hipError_t launch_gemm1_stream(const uint8_t* xq, const uint8_t* xs, const int32
                                const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local, int nt,
                                hipStream_t st);
 hipError_t launch_gemm2_stream(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st);
+                               const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, SingleRows sr,
+                               hipStream_t st);
 // Pair-indexed GEMMs: GEMM1's blocks list their slot's pairs from phys
 // [T*k], read per-token rows xq_tok/xs_tok and write pair rows aq/as
 // [T*k, F]; GEMM2 reads those and writes pair rows y [T*k, H].  T <= 1024.
@@ -88,7 +103,8 @@ hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_
                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
                               hipStream_t st);
 hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
-                              const uint8_t* pw2s, float* y, int H, int F, int P_local, hipStream_t st);
+                              const uint8_t* pw2s, float* y, int H, int F, int P_local, SingleRows sr,
+                              hipStream_t st);
 
 // Router projection (kernels_router.hip): logits [T, E] f32 = x [T, H] bf16 times
 // w_gate [E, H] bf16 transposed.  Plan: blocks of 128 experts x 16 ni tokens

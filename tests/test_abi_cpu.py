@@ -193,3 +193,21 @@ def test_noalloc_entry_validates_on_the_host():
     assert call(_dims(T=600)) == -1
     assert chosen.value == -1  # nothing chosen, nothing launched
     assert "scratch" in mx.moe_status_string(-5)
+
+
+def test_replica_index_and_its_guard():
+    """The remap's replica rule on the host (the kernels use the same
+    function): fmix32(token id) mod rep_count, against the oracle's hash, and a
+    rep_count outside [1, R_max] clamped so the index stays in the table row."""
+    import numpy as np
+    from oracle import moe as om
+    ids = np.array([0, 1, 2, 12345, 2 ** 31 - 1, 2 ** 32 - 1, 987654321], np.uint64)
+    h = om.fmix32(ids).astype(np.int64)
+    for count in (1, 2, 3, 7, 64):
+        got = [mx.moe_replica_of(int(t), count, 64) for t in ids]
+        assert got == list(h % count)
+    for bad, R_max in ((0, 4), (-5, 4), (9, 4), (1000, 64)):
+        for t in ids:
+            r = mx.moe_replica_of(int(t), bad, R_max)
+            assert 0 <= r < R_max
+            assert r == int(om.fmix32(np.array([t], np.uint64))[0]) % min(max(bad, 1), R_max)
