@@ -2,15 +2,19 @@
 """Benchmark: MoE-layer tokens/s of one MI355X's share of the fused MoE layer.
 
 One step = one ``moe_forward`` (route, EPLB remap, quant + dispatch, GEMM1 +
-SwiGLU + requant, GEMM2, combine) over the decode-share workload: 512 tokens,
-d_model 7168, d_ff 2048, 384 experts, top-6 sigmoid routing, 48 local experts
-(one EP8 rank's share), fp8 activations on MXFP4 experts, seeded synthetic
-inputs.  Inputs are resident in HBM before the timed region; the expert
-weights rotate over several device copies so that no step finds them in the
-256 MB MALL or in L2.
+SwiGLU + requant, GEMM2, combine) over one batch of seeded synthetic inputs.
+The headline is the decode share: 512 tokens, d_model 7168, d_ff 2048, 384
+experts, top-6 sigmoid routing, 48 local experts (one EP8 rank's share), fp8
+activations on MXFP4 experts.  The same line carries the 8192-token half of
+the metric: the literal prefill share (8192 tokens into the same 48 experts)
+and the EP-shaped prefill share (8 ranks x 8192 tokens routed into this
+GPU's 48 experts, the load an EP8 rank's experts see), each with the GEMM
+kernels' times measured inside the timed forwards.  Inputs are resident in
+HBM before each timed region; the expert weights rotate over several device
+copies so that no step finds them in the 256 MB MALL or in L2.
 
-Prints ONE JSON line (rank 0).  ``--gpus`` above 1 is refused: this build runs
-on one GPU.
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one
+GPU.
 """
 
 from __future__ import annotations
@@ -43,71 +47,101 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemm1_bytes(d, touched: int, rows: int) -> int:
-    """Algorithmic bytes of one GEMM1 launch: MXFP4 W1 + scales of every touched
-    slot, the fp8 rows and scales read, the requantised rows and scales written."""
-    w = touched * (2 * d.F * d.H // 2 + 2 * d.F * d.H // 32)
-    return w + rows * (d.H + d.H // 128) + rows * (d.F + d.F // 128)
+def w1_bytes(d, touched: int) -> int:
+    """Algorithmic bytes of GEMM1's weights: MXFP4 W1 + scales of every
+    touched slot (15,597,568 B per slot at d_model 7168, d_ff 2048)."""
+    return touched * (2 * d.F * d.H // 2 + 2 * d.F * d.H // 32)
+
+
+def w2_bytes(d, touched: int) -> int:
+    """Algorithmic bytes of GEMM2's weights: MXFP4 W2 + scales of every touched slot."""
+    return touched * (d.H * d.F // 2 + d.H * d.F // 32)
 
 
 def layer_bytes(d, touched: int) -> int:
     """Algorithmic bytes of the layer: all weights of touched slots, and per token
     its logits (f32), input row and output row (bf16)."""
-    w = touched * (2 * d.F * d.H // 2 + 2 * d.F * d.H // 32 + d.H * d.F // 2 + d.H * d.F // 32)
-    return w + d.T * (d.E * 4 + d.H * 2 + d.H * 2)
+    return w1_bytes(d, touched) + w2_bytes(d, touched) + d.T * (d.E * 4 + d.H * 2 + d.H * 2)
 
 
-def run_gpu(workload: str, steps: int, warmup: int, copies: int):
+def layer_flops(d, rows: int) -> int:
+    """Algorithmic flop: 2 (2F H + H F) per local (token, expert) pair."""
+    return 2 * rows * (2 * d.F * d.H + d.H * d.F)
+
+
+def packed_weights(wl, copies: int):
+    """The workload's experts packed once (outside every timed region), plus
+    copies - 1 clones to rotate over."""
     import torch
     import moe_expert_layer_sigmoid_amd as mx
-    import synth
+    d = mx.Dims.of(wl.dims)
+    nat = [torch.from_numpy(a).to("cuda") for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
+    w = [mx.pack_weights(d, *nat)]
+    del nat
+    for _ in range(copies - 1):
+        w.append(tuple(t.clone() for t in w[0]))
+    return w
 
-    t0 = time.time()
-    wl = synth.make(workload)
-    _log(f"[bench] inputs for {workload} generated in {time.time() - t0:.1f}s")
+
+def measure(wl, weights, steps: int, warmup: int, path: str = "auto"):
+    """Time `steps` forwards of workload ``wl`` after `warmup`, the weights
+    rotating over ``weights``: first plain forwards (the step time), then
+    `steps` more that also record HIP events right before and after their
+    GEMM1 and GEMM2 launches (on the stream the kernels run on), which give
+    the GEMM kernels' times inside whole forwards (the events are kept out
+    of the first region: four records inside a forward cost about 10 us of
+    step time).  Returns a dict of the measurements."""
+    import torch
+    import moe_expert_layer_sigmoid_amd as mx
+
     d = mx.Dims.of(wl.dims)
     dev = "cuda"
     x = torch.from_numpy(wl.x.view("int16")).to(dev)
     logits = torch.from_numpy(wl.logits).to(dev)
     rc = torch.from_numpy(wl.rep_count).to(dev)
     rs = torch.from_numpy(wl.rep_slots).to(dev)
-    nat = [torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
-    w = [mx.pack_weights(d, *nat)]     # one-time repack, outside the timed region
-    del nat
-    for _ in range(copies - 1):
-        w.append(tuple(t.clone() for t in w[0]))
     out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
     ws = mx.workspace(d)
     taps = mx.make_taps(d)
-    chosen = mx.moe_forward(d, x, logits, *w[0], rc, rs, out, ws, taps=taps)
+    chosen = mx.moe_forward(d, x, logits, *weights[0], rc, rs, out, ws, taps=taps, path=path)
     torch.cuda.synchronize()
     counts = taps["counts"].cpu().numpy()
-    touched = int((counts > 0).sum())
-    rows = int(counts.sum())
-
-    def step(i):
-        mx.moe_forward(d, x, logits, *w[i % copies], rc, rs, out, ws)
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    touched, rows = int((counts > 0).sum()), int(counts.sum())
+    del taps
+    nw = len(weights)
     st = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for e in [e for four in ev for e in four]:
+        e.record(st)        # creates the HIP event behind each torch event
+    for i in range(warmup):
+        mx.moe_forward(d, x, logits, *weights[i % nw], rc, rs, out, ws, path=path)
+    torch.cuda.synchronize()
     tw0 = time.perf_counter()
-    ev0.record(st)
     for i in range(steps):
         marks[i].record(st)
-        step(i)
+        mx.moe_forward(d, x, logits, *weights[i % nw], rc, rs, out, ws, path=path)
     marks[steps].record(st)
-    ev1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - tw0
-    gpu_ms = ev0.elapsed_time(ev1)
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    for i in range(steps):
+        mx.moe_forward(d, x, logits, *weights[i % nw], rc, rs, out, ws, path=path, gemm_events=ev[i])
+    torch.cuda.synchronize()
+    g1 = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)) / steps
+    g2 = sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(steps)) / steps
+    del ws, out
+    torch.cuda.empty_cache()
+    return dict(d=d, chosen=chosen, touched=touched, rows=rows, wall=wall,
+                gpu_ms=marks[0].elapsed_time(marks[steps]), per_step=per_step,
+                gemm1_us=g1 * 1000.0, gemm2_us=g2 * 1000.0)
 
-    # achievable HBM rate: a plain 1 GiB device-to-device copy (read + write)
-    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+
+def copy_rate_gbs() -> float:
+    """Achievable HBM rate: a plain 1 GiB device-to-device copy (read + write)."""
+    import torch
+    st = torch.cuda.current_stream()
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
@@ -117,31 +151,27 @@ def run_gpu(workload: str, steps: int, warmup: int, copies: int):
         dst.copy_(src)
     c1.record(st)
     torch.cuda.synchronize()
-    copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+    return 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
-    # dominant kernel (GEMM1 of the small-input path: the same kernel the
-    # forward launches) alone, on the stream it is launched on, with the
-    # forward's own intermediates as inputs
-    assert chosen == "small_m", chosen
 
-    def gemm1(i):
-        mx.moe_grouped_gemm1_swiglu_pairs(d, taps["xq_tok"], taps["xs_tok"], taps["phys_ids"], w[i % copies][0],
-                                          w[i % copies][1], taps["aq_pair"], taps["as_pair"], taps["counts"],
-                                          stream=st)
-
-    for i in range(3):
-        gemm1(i)
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record(st)
-    for i in range(steps):
-        gemm1(i)
-    g1.record(st)
-    torch.cuda.synchronize()
-    g1_us = g0.elapsed_time(g1) * 1000.0 / steps
-    return dict(d=d, wl=wl, chosen=chosen, touched=touched, rows=rows, wall=wall, gpu_ms=gpu_ms,
-                gemm1_us=g1_us, per_step=per_step, copy_gbs=copy_gbs)
+def summary(r, label: str):
+    """Per-workload figures: tokens/s, fractions of the HBM roofline (layer
+    bytes) and of the MFMA peak (layer flop), the GEMM kernels' times."""
+    d = r["d"]
+    ms = r["gpu_ms"] / len(r["per_step"])
+    lay, fl = layer_bytes(d, r["touched"]), layer_flops(d, r["rows"])
+    g1, g2 = r["gemm1_us"] * 1e-6, r["gemm2_us"] * 1e-6
+    f1 = 2 * r["rows"] * 2 * d.F * d.H
+    return {"workload": label, "T": d.T, "path": r["chosen"], "touched_slots": r["touched"], "rows": r["rows"],
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(d.T / (ms * 1e-3), 1),
+            "hbm_frac": round(lay / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "gemm1_us": round(r["gemm1_us"], 2), "gemm2_us": round(r["gemm2_us"], 2),
+            "gemm1_mfma_frac": round(f1 / g1 / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "gemm2_mfma_frac": round((fl - f1) / g2 / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "gemms_mfma_frac": round(fl / (g1 + g2) / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "gemm1_weight_gbs": round(w1_bytes(d, r["touched"]) / g1 / 1e9, 1),
+            "gemm2_weight_gbs": round(w2_bytes(d, r["touched"]) / g2 / 1e9, 1)}
 
 
 def _time(fn, steps: int, warmup: int, stream) -> float:
@@ -166,58 +196,17 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
     experts, LARGE_M) and the skewed-routing EPLB share (8192 tokens, 448
     physical slots, 56 local).  One JSON line per point on stdout."""
     import torch
-    import moe_expert_layer_sigmoid_amd as mx
     import synth
 
-    dev = "cuda"
-    st = torch.cuda.current_stream()
-    base = synth.make_sweep(1)
-    d0 = mx.Dims.of(base.dims)
-    nat = [torch.from_numpy(a).to(dev) for a in (base.w1, base.w1s, base.w2, base.w2s)]
-    w = [mx.pack_weights(d0, *nat)]
-    del nat
-    for _ in range(copies - 1):
-        w.append(tuple(t.clone() for t in w[0]))
+    w = packed_weights(synth.make_sweep(1), copies)
 
     def point(wl, name, path="auto", wts=None, extra=None):
-        wts = w if wts is None else wts
-        nw = len(wts)
-        d = mx.Dims.of(wl.dims)
-        x = torch.from_numpy(wl.x.view("int16")).to(dev)
-        logits = torch.from_numpy(wl.logits).to(dev)
-        rc = torch.from_numpy(wl.rep_count).to(dev)
-        rs = torch.from_numpy(wl.rep_slots).to(dev)
-        out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
-        ws = mx.workspace(d)
-        taps = mx.make_taps(d)
-        chosen = mx.moe_forward(d, x, logits, *wts[0], rc, rs, out, ws, taps=taps, path=path)
-        torch.cuda.synchronize()
-        counts = taps["counts"].cpu().numpy()
-        touched, rows = int((counts > 0).sum()), int(counts.sum())
-        ms = _time(lambda i: mx.moe_forward(d, x, logits, *wts[i % nw], rc, rs, out, ws, path=path),
-                   steps, warmup, st)
-        lay = layer_bytes(d, touched)
-        flops = 2 * rows * (2 * d.F * d.H + d.H * d.F)
-        rec = {"point": name, "T": d.T, "path": chosen, "touched_slots": touched, "rows": rows,
-               "ms_per_step": round(ms, 4), "tokens_per_s": round(d.T / (ms * 1e-3), 1),
-               "hbm_frac": round(lay / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-               "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
-        if chosen == "large_m":
-            # the two grouped GEMMs alone, through the component calls (bucketed rows)
-            g1 = _time(lambda i: mx.moe_grouped_gemm1_swiglu(d, taps["xq"], taps["xs"], taps["offsets"],
-                                                             wts[i % nw][0], wts[i % nw][1], taps["aq"],
-                                                             taps["as_"], ws, stream=st), steps, warmup, st)
-            g2c = _time(lambda i: mx.moe_grouped_gemm2_combine(d, taps["aq"], taps["as_"], taps["offsets"],
-                                                               wts[i % nw][2], wts[i % nw][3],
-                                                               taps["row_of_pair"], taps["topk_w"], out, ws,
-                                                               stream=st), steps, warmup, st)
-            f1 = 2 * rows * 2 * d.F * d.H
-            rec.update(gemm1_ms=round(g1, 4), gemm1_mfma_frac=round(f1 / (g1 * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                       gemm2_combine_ms=round(g2c, 4))
+        r = measure(wl, w if wts is None else wts, steps, warmup, path)
+        rec = {"point": name, **summary(r, name)}
+        rec.pop("workload")
         if extra:
-            rec.update(extra(d, ms))
+            rec.update(extra(r["d"], rec["ms_per_step"]))
         print(json.dumps(rec), flush=True)
-        del ws, taps, out
 
     for T in synth.SWEEP_T:
         if only is None or f"sweep_T{T}" in only:
@@ -230,12 +219,7 @@ def run_sweep(steps: int, warmup: int, copies: int, only=None):
         del w[1:]
         torch.cuda.empty_cache()
         wl = synth.make("eplb8192")
-        de = mx.Dims.of(wl.dims)
-        nat = [torch.from_numpy(a).to(dev) for a in (wl.w1, wl.w1s, wl.w2, wl.w2s)]
-        we = [mx.pack_weights(de, *nat)]
-        del nat
-        for _ in range(copies - 1):
-            we.append(tuple(t.clone() for t in we[0]))
+        we = packed_weights(wl, copies)
         point(wl, "eplb8192", wts=we, extra=lambda d, ms: {"P_total": d.P_total, "P_local": d.P_local})
         del we
         torch.cuda.empty_cache()
@@ -424,28 +408,37 @@ def _pct(sorted_vals, p: float) -> float:
 def cpu_baseline(wl, n_slots: int):
     """The oracle (float64 NumPy) on a bounded sample: the whole front end for
     all tokens plus the expert work of the first ``n_slots`` local slots,
-    scaled to the full layer by P_local / n_slots; then the same with BLAS on
-    one thread over one slot."""
+    scaled to the full layer by P_local / n_slots; BLAS on as many threads as
+    the process may use (its CPU affinity), then the same on one thread over
+    one slot."""
     from oracle import moe as om
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas, threadpool_limits = 1, None
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
     d = wl.dims
-    t0 = time.perf_counter()
-    om.forward(wl, slots=range(n_slots))
-    dt = time.perf_counter() - t0
+
+    def run(slots):
+        t0 = time.perf_counter()
+        om.forward(wl, slots=range(slots))
+        return time.perf_counter() - t0
+
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=cores):
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            dt = run(n_slots)
+    else:  # pragma: no cover
+        blas, dt = 1, run(n_slots)
     est = dt * d.P_local / n_slots
-    res = {"value": round(d.T / est, 3), "unit": "tokens/s", "cores": int(blas),
+    res = {"value": round(d.T / est, 3), "unit": "tokens/s", "cores": int(blas), "host_cores": cores,
            "kind": "oracle",
            "sample": f"oracle forward of {d.T} tokens with expert work on {n_slots} of {d.P_local} "
-                     f"local slots ({dt:.1f}s), scaled x{d.P_local / n_slots:g}"}
+                     f"local slots ({dt:.1f}s), scaled x{d.P_local / n_slots:g} to all {d.P_local}; "
+                     f"BLAS on {blas} threads of the {cores} cores this process may use"}
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            om.forward(wl, slots=range(1))
-            dt1 = time.perf_counter() - t0
+            dt1 = run(1)
         res["single_thread"] = {"value": round(d.T / (dt1 * d.P_local), 3), "unit": "tokens/s",
                                 "sample": f"the same with BLAS on one thread and expert work on 1 slot "
                                           f"({dt1:.1f}s), scaled x{d.P_local}"}
@@ -474,6 +467,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated over steps")
     ap.add_argument("--workload", default="decode512", help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="leave out the 8192-token block")
     ap.add_argument("--cpu-slots", type=int, default=8)
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: the token-count sweep and the EP-shaped prefill share, "
@@ -492,8 +486,9 @@ def main():
         run_sweep(args.steps, args.warmup, args.copies,
                   None if args.points is None else set(args.points.split(",")))
         return
+    import torch
+    import synth
     if args.calibrate_copy_mib:
-        import torch
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -502,15 +497,21 @@ def main():
         torch.cuda.synchronize()
         _log(f"[bench] calibration copies: 3 x {n} bytes read and written")
         del src, dst
-    r = run_gpu(args.workload, args.steps, args.warmup, args.copies)
+    t0 = time.time()
+    wl = synth.make(args.workload)
+    _log(f"[bench] inputs for {args.workload} generated in {time.time() - t0:.1f}s")
+    weights = packed_weights(wl, args.copies)
+    r = measure(wl, weights, args.steps, args.warmup)
     d = r["d"]
+    assert r["chosen"] == "small_m", r["chosen"]
     ms = r["wall"] * 1000.0 / args.steps
     value = d.T * args.steps / r["wall"]
-    g1_bytes = gemm1_bytes(d, r["touched"], r["rows"])
+    g1_bytes = w1_bytes(d, r["touched"])
     g1_gbs = g1_bytes / (r["gemm1_us"] * 1e-6) / 1e9
+    g2_gbs = w2_bytes(d, r["touched"]) / (r["gemm2_us"] * 1e-6) / 1e9
     lay_bytes = layer_bytes(d, r["touched"])
-    lay_gbs = lay_bytes / (ms * 1e-3) / 1e9
-    flops = 2 * r["rows"] * (2 * d.F * d.H + d.H * d.F)
+    ev_ms = r["gpu_ms"] / args.steps
+    lay_gbs = lay_bytes / (ev_ms * 1e-3) / 1e9
     line = {
         "metric": "MoE-layer tokens/s per GPU (512 & 8192 tok/rank); % HBM BW / MFMA peak",
         "value": round(value, 1),
@@ -529,20 +530,41 @@ def main():
                    "T": d.T, "H": d.H, "F": d.F, "E": d.E, "k": d.k, "P_local": d.P_local,
                    "path": r["chosen"], "touched_slots": r["touched"], "rows": r["rows"],
                    "weight_copies": args.copies},
+        # the dominant kernel: its algorithmic bytes are the W1 weights (MXFP4 +
+        # scales) of the touched slots; its time is the average of the GEMM1
+        # launches inside the timed forwards (HIP events around the launch)
         "roofline": {"bound": "hbm", "kernel": "k_gemm1_stream<true, 1>", "achieved": round(g1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile("k_gemm1_stream<true, 1>", args.workload),
                      "bytes_per_launch": g1_bytes, "avg_launch_us": round(r["gemm1_us"], 2)},
+        "gemm2": {"kernel": "k_gemm2_stream<true, 1>", "bytes_per_launch": w2_bytes(d, r["touched"]),
+                  "avg_launch_us": round(r["gemm2_us"], 2), "achieved": round(g2_gbs, 1),
+                  "frac": round(g2_gbs / HBM_PEAK_GBS, 4)},
         "layer_roofline": {"bound": "hbm", "achieved": round(lay_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(lay_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": lay_bytes,
-                           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 5),
-                           "gpu_event_ms_per_step": round(r["gpu_ms"] / args.steps, 4),
-                           "measured_copy_gbs": round(r["copy_gbs"], 1)},
+                           "mfma_frac": round(layer_flops(d, r["rows"]) / (ev_ms * 1e-3) / 1e12 /
+                                              FP8_PEAK_TFLOPS, 5),
+                           "gpu_event_ms_per_step": round(ev_ms, 4)},
         "step_ms": {"median": round(_pct(r["per_step"], 50), 4), "p10": round(_pct(r["per_step"], 10), 4),
                     "p90": round(_pct(r["per_step"], 90), 4)},
     }
+    line["layer_roofline"]["measured_copy_gbs"] = round(copy_rate_gbs(), 1)
+    if not args.no_prefill:
+        # the 8192-token half of the metric, on the same experts (weights reused)
+        t0 = time.time()
+        lit = synth.make("prefill8192", with_weights=False)
+        rl = measure(lit, weights, args.steps, args.warmup)
+        ep = synth.make_ep_shaped(8, with_weights=False)
+        _log(f"[bench] prefill inputs generated in {time.time() - t0:.1f}s (timing included)")
+        re_ = measure(ep, weights, args.steps, args.warmup, path="large_m")
+        del ep, lit
+        eps = summary(re_, "EP-shaped prefill share: 8 ranks x 8192 tokens routed into this GPU's 48 experts")
+        eps["rank_share_tokens_per_s"] = round(8192 / (eps["ms_per_step"] * 1e-3), 1)
+        eps["mfma_target"] = {"gemms_mfma_frac": 0.5, "met": eps["gemms_mfma_frac"] >= 0.5}
+        line["prefill"] = {"literal_T8192": summary(rl, "prefill share: 8192 tokens into the 48 local experts"),
+                           "ep8_T65536": eps}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(r["wl"], args.cpu_slots)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_slots)
     print(json.dumps(line), flush=True)
 
 
