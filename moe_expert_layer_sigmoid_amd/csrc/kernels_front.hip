@@ -548,10 +548,12 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(
     const int32_t* __restrict__ rep_count, const int32_t* __restrict__ rep_slots, int R_max,
     uint32_t token_id_base, int P_total, int nr, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ phys, int32_t* __restrict__ partial, uint8_t* __restrict__ xq_tok,
-    uint8_t* __restrict__ xs_tok, const int32_t* __restrict__ t_dev) {
+    uint8_t* __restrict__ xs_tok, const int32_t* __restrict__ t_dev, int32_t* __restrict__ zero, int nzero) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int Tcap = T;
   if (t_dev) T = __builtin_amdgcn_readfirstlane(min(max(*t_dev, 0), Tcap));
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += kFrontThreads) zero[i] = 0;
   if ((int)blockIdx.x < nr) {
     __shared__ int s_rc[1024];
     __shared__ int s_rs[kRepLds];
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(
 hipError_t launch_front(int T, int E, int k, int H, const float* logits, const uint16_t* x, const int32_t* rep_count,
                         const int32_t* rep_slots, int R_max, uint32_t token_id_base, int P_total, int32_t* ids,
                         float* w, int32_t* phys, int32_t* partial, uint8_t* xq_tok, uint8_t* xs_tok,
-                        hipStream_t st, const int32_t* t_dev) {
+                        hipStream_t st, const int32_t* t_dev, int32_t* zero, int nzero) {
   if (T == 0) return hipSuccess;
   const int nr = (T + 15) / 16;
   // xq_tok == NULL: routing blocks only (callers that take bf16 rows)
@@ -618,7 +620,7 @@ hipError_t launch_front(int T, int E, int k, int H, const float* logits, const u
   case N:                                                                                                      \
     k_front<N><<<grid, kFrontThreads, 0, st>>>(T, E, k, H, logits, x, rep_count, rep_slots, R_max,             \
                                                token_id_base, P_total, nr, ids, w, phys, partial, xq_tok,     \
-                                               xs_tok, t_dev);                                                \
+                                               xs_tok, t_dev, zero, nzero);                                   \
     break;
     MOE_ROUTE_CASES(X)
 #undef X
@@ -628,7 +630,8 @@ hipError_t launch_front(int T, int E, int k, int H, const float* logits, const u
 
 // a7 over pair-indexed GEMM2 rows: out[t] = bf16_rne(sum over local j,
 // ascending, of w[t][j] * y[t * k + j]) (the same f32 fma chain as
-// k_combine).  Extra blocks after the ncomb combine blocks finish the load
+// k_combine; y of a pair is the sum of GEMM2's ky K-range partials,
+// ascending, when it split K).  Extra blocks after the ncomb combine blocks finish the load
 // record: nred blocks add the routing blocks' chunk counts into load_hist
 // (64 slots per block, four chunk groups per slot reduced in LDS), and the
 // last block turns the per-slot counts (written by GEMM1) into offsets.
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(256) void k_combine_pairs(int T, int H, int k, cons
                                                        int ncomb, int nred, const int32_t* __restrict__ partial,
                                                        int nch, int P_total, int32_t* __restrict__ load_hist,
                                                        const int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets) {
+                                                       int32_t* __restrict__ offsets, int ky) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= ncomb) {
     const int r = (int)blockIdx.x - ncomb;
@@ -706,8 +709,21 @@ __global__ __launch_bounds__(256) void k_combine_pairs(int T, int H, int k, cons
     const float wj = ws[j];
     if (j >= k || !((local >> j) & 1u)) continue;  // wave-uniform
     const float* yr = y + ((size_t)t * k + j) * H + h;
-    const float4 y0 = *reinterpret_cast<const float4*>(yr);
-    const float4 y1 = *reinterpret_cast<const float4*>(yr + 4);
+    float4 y0 = *reinterpret_cast<const float4*>(yr);
+    float4 y1 = *reinterpret_cast<const float4*>(yr + 4);
+    for (int kk = 1; kk < ky; ++kk) {  // GEMM2's K partials, ascending
+      const float* yk = yr + (size_t)kk * T * k * H;
+      const float4 u0 = *reinterpret_cast<const float4*>(yk);
+      const float4 u1 = *reinterpret_cast<const float4*>(yk + 4);
+      y0.x += u0.x;
+      y0.y += u0.y;
+      y0.z += u0.z;
+      y0.w += u0.w;
+      y1.x += u1.x;
+      y1.y += u1.y;
+      y1.z += u1.z;
+      y1.w += u1.w;
+    }
     a[0] = fmaf(wj, y0.x, a[0]);
     a[1] = fmaf(wj, y0.y, a[1]);
     a[2] = fmaf(wj, y0.z, a[2]);
@@ -727,13 +743,14 @@ __global__ __launch_bounds__(256) void k_combine_pairs(int T, int H, int k, cons
 
 hipError_t launch_combine_pairs(int T, int H, int k, const float* y, const int32_t* phys, int p0, int P_local,
                                 const float* w, uint16_t* out, const int32_t* partial, int nch, int P_total,
-                                int32_t* load_hist, const int32_t* counts, int32_t* offsets, hipStream_t st) {
+                                int32_t* load_hist, const int32_t* counts, int32_t* offsets, hipStream_t st,
+                                int ky) {
   if (T == 0) return hipSuccess;
   const long waves = (long)T * ((H + 511) / 512);
   const int ncomb = (int)((waves + 3) / 4);
   const int nred = load_hist ? (P_total + 63) / 64 : 0;
   k_combine_pairs<<<(unsigned)(ncomb + nred + 1), 256, 0, st>>>(T, H, k, y, phys, p0, P_local, w, out, ncomb, nred,
-                                                                partial, nch, P_total, load_hist, counts, offsets);
+                                                                partial, nch, P_total, load_hist, counts, offsets, ky);
   return hipGetLastError();
 }
 

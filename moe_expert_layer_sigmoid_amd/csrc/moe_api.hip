@@ -20,8 +20,46 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ids, w, phys, rank, partial, base, counts, offsets, rop, por, xq, xs, aq, as, y, plist, rtok, rw, total;
+  size_t ids, w, phys, rank, partial, base, counts, offsets, rop, por, xq, xs, aq, as, y, plist, rtok, rw, kcnt, tlist,
+      total;
 };
+
+// Split K of the pair-indexed GEMMs at decode shares (few touched slots,
+// each otherwise streamed by a few CUs): ks K ranges per block with
+// ks * T <= kSplitRows (measured at 7168 x 2048, top-6 of 384: 1 token
+// 50 -> 39 us, 8 tokens 65 -> 46 us; at 64 tokens a split of 2 was slower).  GEMM1's partials ([ks][T k][2F] f32) and GEMM2's
+// partial y ([ks][T k][H] f32) share the y region, which holds
+// max(T_max, kSplitRows) k rows of H.
+constexpr int kSplitRows = 32;
+size_t y_rows(const moe_dims_t* d) { return (size_t)(d->T_max > kSplitRows ? d->T_max : kSplitRows) * d->k; }
+// (The decode-share form runs with one token tile per pass: none of it
+// where the streaming GEMMs take two.)
+int stream_tiles(const moe_dims_t* d);
+int split_k1(const moe_dims_t* d) {
+  if (d->T <= 0 || stream_tiles(d) >= 2) return 1;
+  const long nq = pack_geom(2u * d->F, (uint32_t)d->H).steps / 4;
+  long ks = kSplitRows / d->T;
+  const long fit = (long)(y_rows(d) * d->H / ((size_t)d->T * d->k * 2 * d->F));  // partials within the y region
+  ks = ks < nq ? ks : nq;
+  ks = ks < fit ? ks : fit;
+  return ks > 1 ? (int)ks : 1;
+}
+// Block rows of the pair-indexed GEMMs: twice the expected number of
+// touched local slots (T k P_local / P_total under uniform routing), at
+// least 8, at most P_local (then every slot has its row, as at large T).
+int touched_rows(const moe_dims_t* d) {
+  if (stream_tiles(d) >= 2) return d->P_local;
+  const long e = ((long)d->T * d->k * d->P_local + d->P_total - 1) / d->P_total;
+  long v = 2 * e > 8 ? 2 * e : 8;
+  return (int)(v < d->P_local ? v : d->P_local);
+}
+int split_k2(const moe_dims_t* d) {
+  if (d->T <= 0 || stream_tiles(d) >= 2) return 1;
+  const long nq = pack_geom((uint32_t)d->H, (uint32_t)d->F).steps / 4;
+  long ks = kSplitRows / d->T;
+  ks = ks < nq ? ks : nq;
+  return ks > 1 ? (int)ks : 1;
+}
 
 // One workspace serves every call; regions are sized by T_max.
 Layout layout_of(const moe_dims_t* d) {
@@ -50,12 +88,16 @@ Layout layout_of(const moe_dims_t* d) {
   L.xs = take(TK * (d->H / kActBlock));
   L.aq = take(TK * d->F);
   L.as = take(TK * (d->F / kActBlock));
-  L.y = take(TK * d->H * 4);
+  L.y = take(y_rows(d) * d->H * 4);
   // per-slot pair lists of the pair-indexed GEMMs (GEMM1 -> GEMM2)
   L.plist = take((size_t)d->P_local * pair_list_stride(d->T_max, d->k) * 4);
   // bucketed rows of single-pair tokens (GEMM2 writes their output rows)
   L.rtok = take(TK * 4);
   L.rw = take(TK * 4);
+  // split-K GEMM1 counters, one per (slot, 128 columns of F)
+  L.kcnt = take((size_t)d->P_local * (d->F / kActBlock) * 4);
+  // the pair-indexed GEMMs' touched-slot list (count, then slots)
+  L.tlist = take(((size_t)d->P_local + 1) * 4);
   L.total = off;
   return L;
 }
@@ -306,8 +348,8 @@ int moe_grouped_gemm1_swiglu_pairs(const moe_dims_t* d, const uint8_t* xq_tok, c
   if (d->T > kPairMaxT) return MOE_ERR_UNSUPPORTED;
   if (d->T == 0) return MOE_OK;
   return hip_status(launch_gemm1_pairs(xq_tok, xs_tok, phys_ids, d->T, d->k, d->p0, pw1, pw1s, aq_pair, as_pair,
-                                       counts, nullptr, 0, d->H, d->F, d->P_local, stream_tiles(d),
-                                       (hipStream_t)stream));
+                                       counts, nullptr, 0, d->H, d->F, d->P_local, stream_tiles(d), 1, nullptr,
+                                       nullptr, d->P_local, nullptr, (hipStream_t)stream));
 }
 
 int moe_grouped_gemm2_combine_pairs(const moe_dims_t* d, const uint8_t* aq_pair, const uint8_t* as_pair,
@@ -324,10 +366,11 @@ int moe_grouped_gemm2_combine_pairs(const moe_dims_t* d, const uint8_t* aq_pair,
   if (d->T == 0) return MOE_OK;
   hipStream_t st = (hipStream_t)stream;
   float* y = at<float>(ws, layout_of(d).y);
+  const int ks2 = split_k2(d);
   MOE_TRY(launch_gemm2_pairs(aq_pair, as_pair, phys_ids, d->T, d->k, d->p0, nullptr, nullptr, 0, pw2, pw2s, y, d->H,
-                             d->F, d->P_local, stream_tiles(d), st));
+                             d->F, d->P_local, stream_tiles(d), ks2, d->P_local, nullptr, st));
   MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys_ids, d->p0, d->P_local, topk_w, out, nullptr, 0,
-                               d->P_total, nullptr, counts, offsets, st));
+                               d->P_total, nullptr, counts, offsets, st, ks2));
   return MOE_OK;
 }
 
@@ -391,22 +434,26 @@ int forward_impl(const moe_dims_t* d, moe_path_t path, const int32_t* t_dev, con
     uint8_t* xs_tok = pick(tp.xs_tok, L.xs);
     uint8_t* aq_p = pick(tp.aq_pair, L.aq);
     uint8_t* as_p = pick(tp.as_pair, L.as);
+    const int ks1 = split_k1(d), ks2 = split_k2(d), nvs = touched_rows(d);
+    int32_t* kcnt = at<int32_t>(ws, L.kcnt);
+    int32_t* tlist = at<int32_t>(ws, L.tlist);
     MOE_TRY(launch_front(d->T, d->E, d->k, d->H, logits, x, rep_count, rep_slots, d->R_max, d->token_id_base,
-                         d->P_total, ids, w, phys, partial, xq_tok, xs_tok, st, t_dev));
+                         d->P_total, ids, w, phys, partial, xq_tok, xs_tok, st, t_dev, ks1 > 1 ? kcnt : nullptr,
+                         ks1 > 1 ? d->P_local * (d->F / kActBlock) : 0));
     const int nt = stream_tiles(d);
     int32_t* plist = at<int32_t>(ws, L.plist);
     const int stride = pair_list_stride(d->T_max, d->k);
     MOE_TRY(mark(tp.gemm1_events[0]));
     MOE_TRY(launch_gemm1_pairs(xq_tok, xs_tok, phys, d->T, d->k, d->p0, pw1, pw1s, aq_p, as_p, counts, plist, stride,
-                               d->H, d->F, d->P_local, nt, st));
+                               d->H, d->F, d->P_local, nt, ks1, y, kcnt, nvs, tlist, st));
     MOE_TRY(mark(tp.gemm1_events[1]));
     MOE_TRY(mark(tp.gemm2_events[0]));
     MOE_TRY(launch_gemm2_pairs(aq_p, as_p, phys, d->T, d->k, d->p0, counts, plist, stride, pw2, pw2s, y, d->H, d->F,
-                               d->P_local, nt, st));
+                               d->P_local, nt, ks2, nvs, tlist, st));
     MOE_TRY(mark(tp.gemm2_events[1]));
     MOE_TRY(launch_combine_pairs(d->T, d->H, d->k, y, phys, d->p0, d->P_local, w, out, partial,
                                  (d->T + kFrontTokens - 1) / kFrontTokens, d->P_total, load_hist, counts, offsets,
-                                 st));
+                                 st, ks2));
     return MOE_OK;
   }
 

@@ -49,17 +49,21 @@ struct SingleRows {
 // chunk counts partial[ceil(T/16), P_total], and every token quantised into
 // xq_tok [T, H] / xs_tok [T, H/128].  t_dev (nullable, device): a token count
 // read on the device; tokens from min(*t_dev, T) on get phys = -1 (idle).
-// xq_tok == NULL: no quantisation blocks (xs_tok ignored).
+// xq_tok == NULL: no quantisation blocks (xs_tok ignored).  zero (nullable):
+// nzero int32 set to 0 (the split-K GEMM1's counters).
 constexpr int kFrontTokens = 16;
 hipError_t launch_front(int T, int E, int k, int H, const float* logits, const uint16_t* x, const int32_t* rep_count,
                         const int32_t* rep_slots, int R_max, uint32_t token_id_base, int P_total, int32_t* ids,
                         float* w, int32_t* phys, int32_t* partial, uint8_t* xq_tok, uint8_t* xs_tok, hipStream_t st,
-                        const int32_t* t_dev = nullptr);
-// Combine of pair rows y [T*k, H], plus load_hist += the front's chunk
-// counts (load_hist nullable) and offsets from the per-slot counts GEMM1 wrote.
+                        const int32_t* t_dev = nullptr, int32_t* zero = nullptr, int nzero = 0);
+// Combine of pair rows y [T*k, H] (the sum over ks of the ky partials at
+// y + ks * T*k*H, ascending, when GEMM2 split K), plus load_hist += the
+// front's chunk counts (load_hist nullable) and offsets from the per-slot
+// counts GEMM1 wrote.
 hipError_t launch_combine_pairs(int T, int H, int k, const float* y, const int32_t* phys, int p0, int P_local,
                                 const float* w, uint16_t* out, const int32_t* partial, int nch, int P_total,
-                                int32_t* load_hist, const int32_t* counts, int32_t* offsets, hipStream_t st);
+                                int32_t* load_hist, const int32_t* counts, int32_t* offsets, hipStream_t st,
+                                int ky = 1);
 
 // GEMM kernels (kernels_gemm.hip).  Weights are in the packed layout of
 // moe_layout.hpp; launch_pack converts one natural MXFP4 matrix set
@@ -86,12 +90,22 @@ inline int pair_list_stride(int T_max, int k) {
   const long tk = (long)T_max * k;
   return (int)(tk < kPairMaxT ? tk : kPairMaxT);
 }
+// Split K (ks_n > 1, at most the number of 1024-element K quads): GEMM1's
+// partial sums go to part [ks_n][T*k][2F] f32 and cnt [P_local * F/128]
+// (zero before the call, left zero) counts finished blocks; GEMM2 writes
+// ks_n partial y at y + ks * T*k*H, which the combine adds.
+// Touched-slot rows (nvs < P_local): nvs block rows instead of P_local, row j
+// taking the touched slots j, j + nvs, ... (ascending slot order); GEMM1 also
+// zeroes the counts of untouched slots and leaves the touched list in tlist
+// [1 + P_local] (count first), from which GEMM2 (with plist) takes its slots.
 hipError_t launch_gemm1_pairs(const uint8_t* xq_tok, const uint8_t* xs_tok, const int32_t* phys, int T, int k, int p0,
                               const uint8_t* pw1, const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int32_t* counts,
-                              int32_t* plist, int stride, int H, int F, int P_local, int nt, hipStream_t st);
+                              int32_t* plist, int stride, int H, int F, int P_local, int nt, int ks_n, float* part,
+                              int32_t* cnt, int nvs, int32_t* tlist, hipStream_t st);
 hipError_t launch_gemm2_pairs(const uint8_t* aq, const uint8_t* as, const int32_t* phys, int T, int k, int p0,
                               const int32_t* counts, const int32_t* plist, int stride, const uint8_t* pw2,
-                              const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, hipStream_t st);
+                              const uint8_t* pw2s, float* y, int H, int F, int P_local, int nt, int ks_n, int nvs,
+                              const int32_t* tlist, hipStream_t st);
 // Large-M: persistent tiled kernels.  Their LDS (operand rings plus the
 // block's token scales) must fit a CU's 160 KB, which holds for
 // H, F <= 8192: tiled_fits(H, F, P_local).

@@ -61,4 +61,43 @@ __device__ __forceinline__ int slot_pairs(const int32_t* __restrict__ phys, int 
   return run;
 }
 
+// The local slots [0, P_local) that hold a pair of phys[0, np) (slot ids
+// from p0 on) as a bitmap in LDS, bits[0, ceil(P_local / 32)); returns how
+// many (the same in every thread).  P_local <= 32 * kTouchedWords.
+constexpr int kTouchedWords = 32;
+__device__ __forceinline__ int touched_bits(const int32_t* __restrict__ phys, int np, int p0, int P_local,
+                                            uint32_t* bits) {
+  const int nw = (P_local + 31) >> 5;
+  for (int i = threadIdx.x; i < nw; i += blockDim.x) bits[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const int p = phys[i] - p0;
+    if (p >= 0 && p < P_local) atomicOr(&bits[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  int n = 0;
+  for (int w = 0; w < nw; ++w) n += __popc(bits[w]);
+  return n;
+}
+// The slot of set bit number j (ascending; 0 <= j < the number set).
+__device__ __forceinline__ int nth_bit(const uint32_t* bits, int P_local, int j) {
+  const int nw = (P_local + 31) >> 5;
+  for (int w = 0; w < nw; ++w) {
+    uint32_t b = bits[w];
+    const int c = __popc(b);
+    if (j < c) {
+      for (; j > 0; --j) b &= b - 1u;
+      return w * 32 + __builtin_ctz(b);
+    }
+    j -= c;
+  }
+  return -1;
+}
+// The number of set bits below slot i.
+__device__ __forceinline__ int bit_rank(const uint32_t* bits, int i) {
+  int r = 0;
+  for (int w = 0; w < (i >> 5); ++w) r += __popc(bits[w]);
+  return r + __popc(bits[i >> 5] & ((1u << (i & 31)) - 1u));
+}
+
 }  // namespace moe

@@ -130,6 +130,18 @@ def test_few_touched_slots(path):
     _full_check(synth.make_custom(T=8, H=3072, F=512, E=64, k=6, P_local=16, p0=8, seed=21), path)
 
 
+def test_decode_split_k_many_touched_slots():
+    # 8 tokens whose 16 experts all lie among this GPU's 32 local slots (of
+    # 512): the decode-share form splits K in both GEMMs and runs 16 block
+    # rows for the ~32 touched slots, so that a row takes several slots in turn
+    wl = synth.make_custom(T=8, H=2048, F=2048, E=512, k=16, P_local=32, p0=0, seed=31)
+    wl.logits[:, 32:] = -30.0
+    res = _full_check(wl, "small_m")
+    assert len(np.unique(res["phys_ids"])) > 16
+    again = P.run_forward(wl, path="small_m")
+    assert np.array_equal(res["out"], again["out"])
+
+
 def test_small_m_at_its_token_limit():
     # 1024 tokens each routed to all 16 experts: every slot lists 1024 pairs,
     # the small-input path's capacity
