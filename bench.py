@@ -533,11 +533,11 @@ def main():
         # the dominant kernel: its algorithmic bytes are the W1 weights (MXFP4 +
         # scales) of the touched slots; its time is the average of the GEMM1
         # launches inside the timed forwards (HIP events around the launch)
-        "roofline": {"bound": "hbm", "kernel": "k_gemm1_stream<true, 1>", "achieved": round(g1_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_gemm1_stream<true, 1, false>", "achieved": round(g1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile("k_gemm1_stream<true, 1>", args.workload),
+                     "traffic": traffic_from_profile("k_gemm1_stream<true, 1, false>", args.workload),
                      "bytes_per_launch": g1_bytes, "avg_launch_us": round(r["gemm1_us"], 2)},
-        "gemm2": {"kernel": "k_gemm2_stream<true, 1>", "bytes_per_launch": w2_bytes(d, r["touched"]),
+        "gemm2": {"kernel": "k_gemm2_stream<true, 1, false>", "bytes_per_launch": w2_bytes(d, r["touched"]),
                   "avg_launch_us": round(r["gemm2_us"], 2), "achieved": round(g2_gbs, 1),
                   "frac": round(g2_gbs / HBM_PEAK_GBS, 4)},
         "layer_roofline": {"bound": "hbm", "achieved": round(lay_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
