@@ -57,7 +57,9 @@ int split_k2(const moe_dims_t* d) {
   if (d->T <= 0 || stream_tiles(d) >= 2) return 1;
   const long nq = pack_geom((uint32_t)d->H, (uint32_t)d->F).steps / 4;
   long ks = kSplitRows / d->T;
+  const long fit = (long)(y_rows(d) / ((size_t)d->T * d->k));  // partial y within the y region
   ks = ks < nq ? ks : nq;
+  ks = ks < fit ? ks : fit;
   return ks > 1 ? (int)ks : 1;
 }
 
