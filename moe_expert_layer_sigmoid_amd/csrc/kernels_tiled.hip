@@ -23,6 +23,10 @@
 //    B-operand reads of a 16-token tile hit distinct banks; a weight tile
 //    (the packed layout is the MFMA operand order) is read back with one
 //    ds_read_b128 per lane.  Weight scales come into registers.
+//  - A stage's DMA is issued by half of the waves (by stage parity), so
+//    that while they wait for the CU's address unit to take it the other
+//    wave of each SIMD runs its MFMAs; the item loop is compiled once per
+//    half, each copy with a fixed DMA pattern.
 //  - Stage barriers are bare s_barrier with explicit vmcnt waits: the
 //    generic workgroup barrier would drain every load in flight.
 //  - Epilogue: GEMM1 SwiGLU + fp8 requant, GEMM2 y rows in f32; its stores
@@ -106,25 +110,30 @@ struct TItem {
   int tl[2];     // the wave's weight tiles: tl[0], tl[0] + 1, tl[1], tl[1] + 1
 };
 
-constexpr int kWaves = 8;                    // waves per block
-constexpr int kRing = 3;                     // ring stages
-constexpr int kAhead = kRing - 1;            // stages in flight ahead of use
-constexpr int kWStage = 32 * 1024;           // weight bytes per stage (32 tiles x 1 KB)
-constexpr int kCols = 256;                   // GEMM1: act columns per item (512 weight rows)
-constexpr int kXI = kStage / 1024 / kWaves;  // token DMA instructions per wave per stage (2)
-constexpr int kWI = 4;                       // weight DMA instructions per wave per stage
-// A stage's DMA is waited for at the start of the stage two later, with one
-// more stage of DMA issued after it; an epilogue's stores follow the DMA of
-// the next item's first two stages (GEMM1: 3 per token tile; GEMM2: 4 of y
-// and 2 of bf16 output rows per token tile).
-constexpr int kVmWait = kXI + kWI;
+constexpr int kWaves = 8;                      // waves per block
+constexpr int kIssuers = kWaves / 2;           // waves that issue one stage's DMA
+constexpr int kRing = 3;                       // ring stages
+constexpr int kAhead = kRing - 1;              // stages in flight ahead of use
+constexpr int kWStage = 32 * 1024;             // weight bytes per stage (32 tiles x 1 KB)
+constexpr int kCols = 256;                     // GEMM1: act columns per item (512 weight rows)
+constexpr int kXI = kStage / 1024 / kIssuers;  // token DMA instructions per issuing wave per stage (4)
+// Each stage's DMA (16 token and 32 weight instructions of 1 KB) is issued by
+// one half of the waves: waves 0-3 for even stages, 4-7 for odd ones, wave
+// u + 4h covering the token pieces u, u + 4, ... and the weight tiles of
+// waves u and u + 4.  A wave stalls while its DMA instructions queue for the
+// CU's address unit (about 900 clocks for a stage's 48); with the issue split
+// by stage parity the other wave of each SIMD runs its MFMAs meanwhile.
+// A stage's DMA is waited for, by the waves that issued it, at the start of
+// the stage two later; they issued nothing in between, except an epilogue's
+// stores (GEMM1: 3 per token tile; GEMM2: 4 of y and 2 of bf16 output rows
+// per token tile), which follow the DMA of the next item's first two stages.
 template <bool G1>
 constexpr int kEpiStores = G1 ? 3 * 8 : 6 * 8;
 // GEMM2's bf16 output rows pass through LDS on their way out: per wave, 16
 // rows of 64 bf16 values with a padded pitch (in the ring slot that no DMA
 // targets at the item's end).
 constexpr int kOutPitch = 144;
-static_assert(kVmWait + kEpiStores<false> <= 63, "vmcnt range");
+static_assert(kEpiStores<false> <= 63, "vmcnt range");
 static_assert(kWaves * 16 * kOutPitch <= kStage + kWStage, "output rows fit one ring slot");
 constexpr size_t kStaticLds = (size_t)kRing * (kStage + kWStage) + kTM * kMaxStages;
 // dynamic LDS: the requant amax, the item prefix and the bucket offsets
@@ -175,13 +184,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
   const int i0 = xcd * chunk, i1 = min(nitems, i0 + chunk);
   if (i0 + lb >= i1) return;  // block-uniform: no item for this block
 
-  uint32_t xt[kXI], xp[kXI];  // token DMA instruction wave + 8m: token row, byte offset of the lane's piece
-#pragma unroll
-  for (int m = 0; m < kXI; ++m) {
-    const int t = 8 * (wave + kWaves * m) + (lane >> 3);
-    xt[m] = (uint32_t)t;
-    xp[m] = 16u * (uint32_t)((lane & 7) ^ swz(t & 15));
-  }
+  // token DMA instruction u + 4m of an issuing wave (u = wave & 3) moves
+  // rows 8 (u + 4m) .. + 7: the lane's row is xt0 + 32m, its piece's byte
+  // offset xp (row & 15 does not depend on m)
+  const int iu = wave & (kIssuers - 1), igrp = wave / kIssuers;
+  const uint32_t xt0 = (uint32_t)(8 * iu + (lane >> 3));
+  const uint32_t xp = 16u * (uint32_t)((lane & 7) ^ swz((int)(xt0 & 15)));
   const uint32_t wlane = 16u * lane, slane = 8u * lane;
   const uint32_t wlim = (uint32_t)Gm.data_slot, slim = (uint32_t)Gm.scale_slot;
 
@@ -222,28 +230,46 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
     return it;
   };
 
-  auto dma_x = [&](const TItem it, uint8_t* slot, int q) {  // token stage q
+  auto dma_x = [&](const TItem it, uint8_t* slot, int q) {  // this wave's token pieces of stage q
     const bool live = it.live && q < nst;
     const uint32_t xlim = (uint32_t)it.nvalid * (uint32_t)K;
     const rsrc_t Xr = make_rsrc(xq + (size_t)it.r0 * K, xlim);
 #pragma unroll
     for (int m = 0; m < kXI; ++m) {
-      const uint32_t vo = (live && xt[m] < (uint32_t)it.nvalid) ? xt[m] * (uint32_t)K + xp[m] : xlim;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (lds_ptr_t)(slot + (wave + kWaves * m) * 1024), 16, vo,
+      const uint32_t t = xt0 + 32u * (uint32_t)m;
+      const uint32_t vo = (live && t < (uint32_t)it.nvalid) ? t * (uint32_t)K + xp : xlim;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (lds_ptr_t)(slot + (iu + kIssuers * m) * 1024), 16, vo,
                                                live ? (uint32_t)q * 128u : 0u, 0, 0);
     }
   };
   // Loads of nothing (no item, no tiles, past K) go through a zero-sized
   // buffer, so the lane offsets stay loop constants.
-  auto dma_w = [&](const TItem it, uint8_t* slot, int q) {  // this wave's four weight tiles of stage q
-    const bool live = it.wlive && q < nst;
-    const rsrc_t Wr = make_rsrc(pw + (size_t)it.s * Gm.data_slot, live ? wlim : 0u);
+  auto dma_w = [&](const TItem it, uint8_t* slot, int q) {  // the weight tiles of waves iu and iu + 4, stage q
     const uint32_t so = (uint32_t)(q >> 1) * 2048u + (uint32_t)(q & 1) * 1024u;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const uint32_t tile = (uint32_t)(((a >> 1) ? it.tl[1] : it.tl[0]) + (a & 1));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(Wr, (lds_ptr_t)(slot + wave * 4096 + a * 1024), 16, wlane,
-                                               live ? tile * (uint32_t)Gm.data_tile + so : 0u, 0, kWeightNt);
+    for (int h = 0; h < 2; ++h) {
+      const int w = iu + kIssuers * h;
+      int t0, t1;
+      bool wl;
+      if (G1) {
+        const int c0 = it.wb * kCols + w * 32;  // wave w's 32 columns of F: gate tiles t0, t0 + 1, up t1, t1 + 1
+        wl = c0 < F;
+        t0 = c0 / 16;
+        t1 = (F + c0) / 16;
+      } else {
+        const int h0 = it.wb * 2 * kCols + w * 64;  // wave w's 64 rows of H: tiles t0 .. t0 + 3
+        wl = h0 < H;
+        t0 = h0 / 16;
+        t1 = t0 + 2;
+      }
+      const bool live = it.live && wl && q < nst;
+      const rsrc_t Wr = make_rsrc(pw + (size_t)it.s * Gm.data_slot, live ? wlim : 0u);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t tile = (uint32_t)(((a >> 1) ? t1 : t0) + (a & 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(Wr, (lds_ptr_t)(slot + w * 4096 + a * 1024), 16, wlane,
+                                                 live ? tile * (uint32_t)Gm.data_tile + so : 0u, 0, kWeightNt);
+      }
     }
   };
   // the four tiles' scales of group grp (stages 8 grp .. 8 grp + 7): byte q % 8 scales stage q
@@ -364,6 +390,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
 
   auto ring = [&](int i) -> uint8_t* { return i == 0 ? g0s : (i == 1 ? g1s : g2s); };  // a select: no table of LDS addresses
 
+  // The item loop in one copy per half of the waves (GRP = wave / 4), so that
+  // each copy's DMA pattern is fixed: the compiler's waits for the weight
+  // scales then count the DMA issued after them instead of draining it.
+  auto run = [&](auto grpc) {
+  constexpr int GRP = decltype(grpc)::value;
   // ---- first item: its token scales, first scale group and first stages
   TItem cur = decode(i0 + lb);
   bool after_epi = false;  // an epilogue's stores are in flight (every item but the first)
@@ -377,8 +408,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kAhead; ++q) {
-    dma_x(cur, ring(q), q);
-    dma_w(cur, ring(q) + kStage, q);
+    if ((q & 1) == GRP) {
+      dma_x(cur, ring(q), q);
+      dma_w(cur, ring(q) + kStage, q);
+    }
   }
   int slot = 0;  // ring slot of the current stage
 
@@ -389,14 +422,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) acc[i][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // one stage: wait for its DMA (own, then everyone's via the barrier,
-    // which also retires the slot the next DMA refills), issue stage q + 2
-    // (of this item or, past its end, of the next), compute stage q
-    auto stage = [&](int q) {
-      if (after_epi && q < kAhead)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kVmWait + kEpiStores<G1>) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kVmWait) : "memory");
+    // one stage (q of parity P): its issuing waves wait for its DMA, the
+    // barrier makes it everyone's (and retires the slot the next DMA
+    // refills); the same waves issue stage q + 2 (of this item or, past its
+    // end, of the next); every wave computes stage q
+    auto stage = [&](int q, auto pc) {
+      constexpr int P = decltype(pc)::value;
+      constexpr bool iss = GRP == P;
+      if constexpr (iss) {
+        if (after_epi && q < kAhead)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kEpiStores<G1>) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       bare_barrier();
       if ((q & 7) == 0) {
 #pragma unroll
@@ -409,30 +447,34 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
         if ((q >> 3) + 1 < ngrp && 8 * ((q >> 3) + 1) < nst4) load_scales(cur, (q >> 3) + 1, scn);
         else load_scales(nxt, 0, scn);
       }
-      uint8_t* const fill = ring(slot == 0 ? kRing - 1 : slot - 1);  // the slot read by stage q - 1
-      if (q + kAhead < nst4) {
-        dma_x(cur, fill, q + kAhead);
-        dma_w(cur, fill + kStage, q + kAhead);
-      } else {
-        dma_x(nxt, fill, q + kAhead - nst4);
-        dma_w(nxt, fill + kStage, q + kAhead - nst4);
+      if constexpr (iss) {
+        uint8_t* const fill = ring(slot == 0 ? kRing - 1 : slot - 1);  // the slot read by stage q - 1
+        if (q + kAhead < nst4) {
+          dma_x(cur, fill, q + kAhead);
+          dma_w(cur, fill + kStage, q + kAhead);
+        } else {
+          dma_x(nxt, fill, q + kAhead - nst4);
+          dma_w(nxt, fill + kStage, q + kAhead - nst4);
+        }
       }
       compute(cur.wlive, ring(slot), ring(slot) + kStage, q);
       slot = slot == kRing - 1 ? 0 : slot + 1;
     };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     for (int q0 = 0; q0 < nst4 - 4; q0 += 4) {
-      stage(q0);
-      stage(q0 + 1);
-      stage(q0 + 2);
-      stage(q0 + 3);
+      stage(q0, P0{});
+      stage(q0 + 1, P1{});
+      stage(q0 + 2, P0{});
+      stage(q0 + 3, P1{});
     }
     uint32_t xsn[kXsPer];
     xs_fetch(nxt, xsn);
     const int rinfn = rinf_fetch(nxt);
-    stage(nst4 - 4);
-    stage(nst4 - 3);
-    stage(nst4 - 2);
-    stage(nst4 - 1);
+    stage(nst4 - 4, P0{});
+    stage(nst4 - 3, P1{});
+    stage(nst4 - 2, P0{});
+    stage(nst4 - 1, P1{});
 
     if (!G1) {
       // ---- GEMM2 epilogue.  Rows of tokens with two or more local pairs (all
@@ -535,6 +577,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
     MOE_LGKM_WAIT(0);
     cur = nxt;
   }
+  };
+  if (igrp == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 }
 
 // Compute units of the current device, looked up once per device.
