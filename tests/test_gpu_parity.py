@@ -85,6 +85,17 @@ def test_tiled_skewed_slots():
     assert res["counts"].max() > 512 and res["chosen"] == "large_m"
 
 
+@pytest.mark.parametrize("path", ["staged", "large_m"])
+def test_bucket_ranks_when_every_pair_collides(path):
+    # k = E = 16 over 24 slots (8 replicas): every token routes to every
+    # expert, so a 64-token chunk holds 1024 pairs (sixteen 64-pair groups of
+    # the bucketed count kernel) and each unreplicated slot gets 64 of them:
+    # ranks 0..63 within every chunk, carried from group to group
+    wl = synth.make_custom(T=200, H=256, F=256, E=16, k=16, P_local=10, p0=7, redundant=8, ranks=2, seed=31)
+    res = _full_check(wl, path)
+    assert res["counts"].max() == 200
+
+
 # At the widest rows the outputs cover ~10^6 elements, and a few of those just
 # above the elementwise floor (1e-3) sit below the block-scaled MFMA's own
 # accumulation error; those elements are held to that bound (2^-14 of the
