@@ -134,18 +134,23 @@ struct SStage {
 };
 
 // Operands of K step st; `gofs` moves the weight tiles to another group of
-// the wave's tiles (a uniform byte offset).
+// the wave's tiles (a uniform byte offset).  dead: a load past the stream's
+// last step, issued only to keep the loop free of branches and never used;
+// it goes through a zero-sized buffer (no memory access, zeros back at once)
+// so that a later wait for the stream's loads does not wait for a re-read.
 template <int WAUX, int NT, bool UT>
-__device__ __forceinline__ void s_load(SStage<NT>& S, const SOps<NT, UT>& O, int st, uint32_t gofs = 0) {
+__device__ __forceinline__ void s_load(SStage<NT>& S, const SOps<NT, UT>& O, int st, uint32_t gofs = 0,
+                                       bool dead = false) {
   const uint32_t wo = (uint32_t)st * 2048 + gofs, xo = (uint32_t)st * 256;
+  const rsrc_t W = dead ? make_rsrc(nullptr, 0u) : O.w;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     if constexpr (UT) {
-      S.a[rt][0] = buf_load16_p<WAUX>(O.w, O.wl, O.wt[rt] + wo);
-      S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wl, O.wt[rt] + wo + 1024);
+      S.a[rt][0] = buf_load16_p<WAUX>(W, O.wl, O.wt[rt] + wo);
+      S.a[rt][1] = buf_load16_p<WAUX>(W, O.wl, O.wt[rt] + wo + 1024);
     } else {
-      S.a[rt][0] = buf_load16_p<WAUX>(O.w, O.wt[rt], wo);
-      S.a[rt][1] = buf_load16_p<WAUX>(O.w, O.wt[rt] + 1024, wo);
+      S.a[rt][0] = buf_load16_p<WAUX>(W, O.wt[rt], wo);
+      S.a[rt][1] = buf_load16_p<WAUX>(W, O.wt[rt] + 1024, wo);
     }
   }
   // Steps past K (the packed weights pad K to a multiple of 1024) take zero
@@ -155,7 +160,7 @@ __device__ __forceinline__ void s_load(SStage<NT>& S, const SOps<NT, UT>& O, int
   // multiple of 128), so the test is uniform.
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const bool live = xo + (uint32_t)i * 128 < O.kx;
+    const bool live = !dead && xo + (uint32_t)i * 128 < O.kx;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const uint32_t b = live ? O.xlo[n] : O.lim;
@@ -206,7 +211,8 @@ __device__ __forceinline__ void s_mma(v4f (&acc)[4][NT], const SStage<NT>& S, co
 // Operand stages run two steps ahead and scale quads one quad ahead across
 // group boundaries (each quad's scales issued before the previous quad's
 // operand loads), so the pipeline never drains between quads or groups; the loop has
-// no branches (its last loads re-read the final steps and are never used).
+// no branches (its last loads, past the final step, go through a zero-sized
+// buffer and are never used).
 // After a group's last step epi(g, acc) consumes its results and acc restarts
 // at zero.  WAUX: cache policy of the weight loads.  The S4 steps are steps
 // st0 .. st0 + S4 - 1 of K (st0 a multiple of 4: a range of whole quads).
@@ -217,9 +223,11 @@ __device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT, 
   SScales c0, c1;
   const int nq = S4 / 4, NQ = G * nq, V = G * S4;
   static_assert(G == 1 || G == 2, "one or two groups");
-  auto ld = [&](SStage<NT>& S, int v) {
-    const int g = (G > 1 && v >= S4) ? 1 : 0;
-    s_load<WAUX>(S, O, st0 + v - g * S4, g ? gd : 0u);
+  auto ld = [&](SStage<NT>& S, int v) {  // v >= V: a dead load (past the stream's end)
+    const bool dead = v >= V;
+    const int vv = dead ? V - 1 : v;
+    const int g = (G > 1 && vv >= S4) ? 1 : 0;
+    s_load<WAUX>(S, O, st0 + vv - g * S4, g ? gd : 0u, dead);
   };
   auto ldsc = [&](SScales& C, int q) {
     const int g = (G > 1 && q >= nq) ? 1 : 0;
@@ -245,13 +253,13 @@ __device__ __forceinline__ void stream_groups(v4f (&acc)[4][NT], const SOps<NT, 
         sb1[n] = *reinterpret_cast<const int*>(O.sxs[n] + 2 * (st0 + st) + 4);
       }
       s_mma<0>(acc, s0, c0, sb0);
-      ld(s0, min(v + 2, V - 2));
+      ld(s0, v + 2);
       s_mma<1>(acc, s1, c0, sb0);
-      ld(s1, min(v + 3, V - 1));
+      ld(s1, v + 3);
       s_mma<2>(acc, s0, c0, sb1);
-      ld(s0, min(v + 4, V - 2));
+      ld(s0, v + 4);
       s_mma<3>(acc, s1, c0, sb1);
-      ld(s1, min(v + 5, V - 1));
+      ld(s1, v + 5);
     }
     epi(g, acc);
 #pragma unroll
