@@ -31,9 +31,10 @@
 //    generic workgroup barrier would drain every load in flight.
 //  - Epilogue: GEMM1 SwiGLU + fp8 requant, GEMM2 y rows in f32; its stores
 //    are issued after the next item's first DMA, whose waits do not drain
-//    them.  (Measured at the EP-shaped prefill share: per item the K loop
-//    runs at 63-67 % of the MFMA rate; GEMM2's items are short, K = 2048,
-//    and its y-store epilogue, all CUs writing at once, is a quarter of each.)
+//    them.  (Measured at the EP-shaped prefill share: stages of ~2750 clocks
+//    for 2048 clocks of MFMA per SIMD; GEMM2's items are short, K = 2048,
+//    and its epilogue, ~1 GB of y and output rows per call, is a fifth of
+//    each item.)
 
 #include <atomic>
 #include <mutex>
@@ -124,9 +125,10 @@ constexpr int kXI = kStage / 1024 / kIssuers;  // token DMA instructions per iss
 // CU's address unit (about 900 clocks for a stage's 48); with the issue split
 // by stage parity the other wave of each SIMD runs its MFMAs meanwhile.
 // A stage's DMA is waited for, by the waves that issued it, at the start of
-// the stage two later; they issued nothing in between, except an epilogue's
-// stores (GEMM1: 3 per token tile; GEMM2: 4 of y and 2 of bf16 output rows
-// per token tile), which follow the DMA of the next item's first two stages.
+// the stage two later (vmcnt 0: their weight-scale loads of the stage between
+// are waited for with it), except that an epilogue's stores (GEMM1: 3 per
+// token tile; GEMM2: 4 of y and 2 of bf16 output rows per token tile) follow
+// the DMA of the next item's first two stages and stay in flight.
 template <bool G1>
 constexpr int kEpiStores = G1 ? 3 * 8 : 6 * 8;
 // GEMM2's bf16 output rows pass through LDS on their way out: per wave, 16
