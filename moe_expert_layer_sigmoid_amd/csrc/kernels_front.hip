@@ -340,7 +340,9 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
                                                const int32_t* __restrict__ phys, int p0, int P_local,
                                                const int32_t* __restrict__ base, const int32_t* __restrict__ rank,
                                                uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                               int32_t* __restrict__ row_of_pair, int32_t* __restrict__ pair_of_row) {
+                                               int32_t* __restrict__ row_of_pair, int32_t* __restrict__ pair_of_row,
+                                               const float* __restrict__ w, int32_t* __restrict__ rtok,
+                                               float* __restrict__ rw) {
   const int lane = threadIdx.x & 63;
   const int nb = H / kActBlock;
   const int ng = (H + 512 * kQC - 1) / (512 * kQC);
@@ -357,6 +359,13 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
       if (grp == 0) pair_of_row[myrow] = (int32_t)pr;
     }
     if (grp == 0) row_of_pair[pr] = myrow;
+  }
+  if (rtok && grp == 0) {  // the single-pair row map (as k_single_rows)
+    const int nloc = __popcll(__ballot(myrow >= 0));
+    if (myrow >= 0) {
+      rtok[myrow] = nloc == 1 ? t : -1;
+      rw[myrow] = w[(size_t)t * k + lane];
+    }
   }
   int rows[16];
   bool any = false;
@@ -395,12 +404,12 @@ __global__ __launch_bounds__(256) void k_quant(int T, int H, int k, const uint16
 
 hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* phys, int p0, int P_local,
                         const int32_t* base, const int32_t* rank, uint8_t* xq, uint8_t* xs, int32_t* row_of_pair,
-                        int32_t* pair_of_row, hipStream_t st) {
+                        int32_t* pair_of_row, hipStream_t st, const float* w, int32_t* rtok, float* rw) {
   if (T == 0) return hipSuccess;
   const int ng = (H + 512 * kQC - 1) / (512 * kQC);
   const long waves = (long)T * ng;
   k_quant<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(T, H, k, x, phys, p0, P_local, base, rank, xq, xs,
-                                                       row_of_pair, pair_of_row);
+                                                       row_of_pair, pair_of_row, w, rtok, rw);
   return hipGetLastError();
 }
 

@@ -463,18 +463,18 @@ int forward_impl(const moe_dims_t* d, moe_path_t path, const int32_t* t_dev, con
   MOE_TRY(launch_count(d->T, d->k, ids, rep_count, rep_slots, d->R_max, d->token_id_base, phys, true, d->P_total,
                        d->p0, d->P_local, partial, rank, st));
   MOE_TRY(launch_scan(nchunks(d->T), d->P_total, d->p0, d->P_local, partial, counts, offsets, base, load_hist, st));
-  MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys, d->p0, d->P_local, base, rank, xq, xs, rop, por, st));
+  // GEMM2 writes the output rows of single-pair tokens itself (their row
+  // map from the quantise pass) whenever the output's byte offsets fit its
+  // 32-bit buffer offsets
+  const bool fuse = (uint64_t)d->T * (uint64_t)d->H * 2u < (1ull << 32);
+  int32_t* rtok = fuse ? at<int32_t>(ws, L.rtok) : nullptr;
+  float* rw = fuse ? at<float>(ws, L.rw) : nullptr;
+  MOE_TRY(launch_quant(d->T, d->H, d->k, x, phys, d->p0, d->P_local, base, rank, xq, xs, rop, por, st, w, rtok, rw));
   MOE_TRY(mark(tp.gemm1_events[0]));
   MOE_TRY(gemm1(p, xq, xs, offsets, pw1, pw1s, aq, as, d, st));
   MOE_TRY(mark(tp.gemm1_events[1]));
-  const bool fuse = (uint64_t)d->T * (uint64_t)d->H * 2u < (1ull << 32);
   SingleRows sr{nullptr, nullptr, nullptr, 0u};
-  if (fuse) {
-    int32_t* rtok = at<int32_t>(ws, L.rtok);
-    float* rw = at<float>(ws, L.rw);
-    MOE_TRY(launch_single_rows(d->T, d->k, rop, w, rtok, rw, st));
-    sr = SingleRows{rtok, rw, out, (uint32_t)((uint64_t)d->T * d->H * 2u)};
-  }
+  if (fuse) sr = SingleRows{rtok, rw, out, (uint32_t)((uint64_t)d->T * d->H * 2u)};
   MOE_TRY(mark(tp.gemm2_events[0]));
   MOE_TRY(gemm2(p, aq, as, offsets, pw2, pw2s, y, sr, d, st));
   MOE_TRY(mark(tp.gemm2_events[1]));

@@ -24,9 +24,12 @@ hipError_t launch_scan(int nch, int P_total, int p0, int P_local, const int32_t*
                        int32_t* offsets, int32_t* base, int32_t* load_hist, hipStream_t st);
 
 // Row assignment + fp8 quantisation + dispatch of each token to its local rows.
+// rtok (nullable): also the single-pair row map launch_single_rows writes
+// (rtok / rw from the routing weights w).
 hipError_t launch_quant(int T, int H, int k, const uint16_t* x, const int32_t* phys, int p0, int P_local,
                         const int32_t* base, const int32_t* rank, uint8_t* xq, uint8_t* xs,
-                        int32_t* row_of_pair, int32_t* pair_of_row, hipStream_t st);
+                        int32_t* row_of_pair, int32_t* pair_of_row, hipStream_t st, const float* w = nullptr,
+                        int32_t* rtok = nullptr, float* rw = nullptr);
 
 // skip_single: leave tokens with exactly one local pair alone (the bucketed
 // GEMM2 kernels wrote their rows, given launch_single_rows's row map).
