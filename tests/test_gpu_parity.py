@@ -124,6 +124,19 @@ def test_widest_rows_tiled(H, F):
     assert res["chosen"] == "large_m"
 
 
+@pytest.mark.parametrize("E,k,T", [(384, 6, 203), (1024, 16, 37), (40, 3, 17)])
+def test_routing_identical_on_both_fronts(E, k, T):
+    # the fused small-input front routes one token per wavefront, the routing
+    # pass of the bucketed paths one token per 16-lane row: the same choices
+    # and the same weights, bit for bit (ragged last rows included)
+    wl = synth.make_custom(T=T, H=256, F=128, E=E, k=k, P_local=8, p0=0, seed=41)
+    a = P.run_forward(wl, path="small_m")
+    b = P.run_forward(wl, path="large_m")
+    assert a["chosen"] == "small_m" and b["chosen"] == "large_m"
+    for n in ("topk_ids", "topk_w", "phys_ids"):
+        assert np.array_equal(a[n], b[n]), n
+
+
 @pytest.mark.parametrize("path", ["auto", "staged"])
 def test_wide_k_and_many_experts(path):
     # k = 16 of 1024 experts (16 logits per lane), skewed popularity; staged:
