@@ -276,11 +276,17 @@ hipError_t launch_count(int T, int k, const int32_t* ids, const int32_t* rep_cou
 }
 
 // ---------------------------------------------------------------------------
-// a2 / a3 (part 2): one block of 1024 threads sums the chunk partials.
-// Local slots: counts, exclusive-scan offsets, and per-(chunk, slot) base rows.
-// All slots: load_hist += totals.  Work is split as (slot, chunk-range) so the
-// serial part per thread is nch / NG loads.
+// a2 / a3 (part 2): blocks of 1024 threads sum the chunk partials.  Block 0,
+// local slots: counts, exclusive-scan offsets, and per-(chunk, slot) base
+// rows, the work split as (slot, chunk-range) so the serial part per thread
+// is nch / NG loads.  Blocks 1.., all slots: load_hist += totals, 64 slots
+// per block, each slot's chunks split over 16 threads (integer sums: the
+// result does not depend on the split).  The loops over chunks keep up to
+// kScanBatch independent loads in flight (one load per step waited for each
+// line in turn).
 // ---------------------------------------------------------------------------
+constexpr int kHistSlotsPerBlock = 64;
+constexpr int kScanBatch = 16;  // chunk loads a thread keeps in flight
 __global__ __launch_bounds__(1024) void k_scan(int nch, int P_total, int p0, int P_local,
                                                const int32_t* __restrict__ partial, int32_t* __restrict__ counts,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ base,
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(1024) void k_scan(int nch, int P_total, int p0, int
   __shared__ int s_part[1024];
   __shared__ int s_tot[1024];
   const int tid = threadIdx.x;
-  if (counts) {
+  if (counts && blockIdx.x == 0) {
     // NG thread groups per local slot; P_local <= 1024
     int NG = 1024 / P_local;
     if (NG > nch) NG = nch;
@@ -299,7 +305,13 @@ __global__ __launch_bounds__(1024) void k_scan(int nch, int P_total, int p0, int
     const int c0 = g * per, c1 = min(nch, c0 + per);
     int sum = 0;
     if (act)
-      for (int c = c0; c < c1; ++c) sum += partial[(size_t)c * P_total + p0 + s];
+      for (int c = c0; c < c1; c += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? partial[(size_t)(c + u) * P_total + p0 + s] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) sum += v[u];
+      }
     if (act) s_part[g * P_local + s] = sum;
     __syncthreads();
     if (tid < P_local) {  // exclusive prefix over groups, total per slot
@@ -329,24 +341,45 @@ __global__ __launch_bounds__(1024) void k_scan(int nch, int P_total, int p0, int
     if (act) {
       // offsets[s] (exclusive prefix of slot totals) + counts of earlier chunk groups
       int run = (s > 0 ? s_tot[s - 1] : 0) + s_part[g * P_local + s];
-      for (int c = c0; c < c1; ++c) {
-        base[(size_t)c * P_local + s] = run;
-        run += partial[(size_t)c * P_total + p0 + s];
+      for (int c = c0; c < c1; c += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? partial[(size_t)(c + u) * P_total + p0 + s] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+          if (c + u < c1) base[(size_t)(c + u) * P_local + s] = run;
+          run += v[u];
+        }
       }
     }
   }
-  if (load_hist) {
-    for (int q = tid; q < P_total; q += 1024) {
-      int sum = 0;
-      for (int c = 0; c < nch; ++c) sum += partial[(size_t)c * P_total + q];
-      load_hist[q] += sum;
+  if (load_hist && blockIdx.x > 0) {
+    constexpr int NG = 1024 / kHistSlotsPerBlock;
+    const int q = ((int)blockIdx.x - 1) * kHistSlotsPerBlock + tid % kHistSlotsPerBlock, g = tid / kHistSlotsPerBlock;
+    int sum = 0;
+    if (q < P_total)
+      for (int c = g; c < nch; c += kScanBatch * NG) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+          v[u] = c + u * NG < nch ? partial[(size_t)(c + u * NG) * P_total + q] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) sum += v[u];
+      }
+    s_part[tid] = sum;
+    __syncthreads();
+    if (tid < kHistSlotsPerBlock && q < P_total) {
+      int tot = 0;
+      for (int gg = 0; gg < NG; ++gg) tot += s_part[gg * kHistSlotsPerBlock + tid];
+      load_hist[q] += tot;
     }
   }
 }
 
 hipError_t launch_scan(int nch, int P_total, int p0, int P_local, const int32_t* partial, int32_t* counts,
                        int32_t* offsets, int32_t* base, int32_t* load_hist, hipStream_t st) {
-  k_scan<<<1, 1024, 0, st>>>(nch, P_total, p0, P_local, partial, counts, offsets, base, load_hist);
+  const unsigned nhist = load_hist ? (unsigned)((P_total + kHistSlotsPerBlock - 1) / kHistSlotsPerBlock) : 0u;
+  k_scan<<<1 + nhist, 1024, 0, st>>>(nch, P_total, p0, P_local, partial, counts, offsets, base, load_hist);
   return hipGetLastError();
 }
 
