@@ -92,10 +92,13 @@ __device__ __forceinline__ v2i lds_read8(const void* p) {
 #define MOE_LGKM_WAIT(n) asm volatile("s_waitcnt lgkmcnt(" #n ")" ::: "memory")
 // Arguments of __builtin_amdgcn_raw_ptr_buffer_load_lds: (buffer, LDS base,
 // bytes per lane, voffset, soffset, immediate offset, cache policy).
-// Weights load with the default cache policy: each weight stage is read by
+// Weight cache policy (a kernel template argument, WNT): the default when the
+// slots have several token blocks, since each weight stage is then read by
 // every token block of the slot (non-temporal loads dropped the L2 hit rate
-// from 77 % to 53 %).
-constexpr int kWeightNt = 0;
+// from 77 % to 53 % at ~1000 rows per slot and cost 3 % there); non-temporal
+// when a slot's rows fit about one block, where nothing re-reads the weights
+// (GEMM1 -5 % at 62 rows per slot).
+constexpr int kWeightNtLoads = 2;
 
 union V8T {
   v8i v;
@@ -141,7 +144,7 @@ constexpr size_t kStaticLds = (size_t)kRing * (kStage + kWStage) + kTM * kMaxSta
 // dynamic LDS: the requant amax, the item prefix and the bucket offsets
 static size_t tiled_lds(int P_local) { return kWaves * kTM * sizeof(float) + 2 * (size_t)(P_local + 1) * sizeof(int); }
 
-template <bool G1>
+template <bool G1, int WNT>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                         const int32_t* __restrict__ offsets, int P_local,
                                                         const uint8_t* __restrict__ pw, const uint8_t* __restrict__ pws,
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_tiled(const uint8_t* __restr
       for (int a = 0; a < 4; ++a) {
         const uint32_t tile = (uint32_t)(((a >> 1) ? t1 : t0) + (a & 1));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(Wr, (lds_ptr_t)(slot + w * 4096 + a * 1024), 16, wlane,
-                                                 live ? tile * (uint32_t)Gm.data_tile + so : 0u, 0, kWeightNt);
+                                                 live ? tile * (uint32_t)Gm.data_tile + so : 0u, 0, WNT);
       }
     }
   };
@@ -623,28 +626,31 @@ static hipError_t grant_lds(const void* fn, size_t lds, size_t (&granted)[kMaxDe
   return hipSuccess;
 }
 
+template <bool G1, int WNT>
+static hipError_t run_tiled(const uint8_t* x, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw,
+                            const uint8_t* pws, uint8_t* aq, uint8_t* as, float* y, int H, int F, int P_local,
+                            SingleRows sr, hipStream_t st) {
+  const size_t lds = tiled_lds(P_local);
+  static size_t granted[kMaxDevices] = {};  // one table per kernel instantiation
+  hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_tiled<G1, WNT>), lds, granted);
+  if (e != hipSuccess) return e;
+  k_tiled<G1, WNT><<<num_cus() / 8 * 8, kWaves * 64, lds, st>>>(x, xs, offsets, P_local, pw, pws, aq, as, y, H, F, sr);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
-                              hipStream_t st) {
-  const size_t lds = tiled_lds(P_local);
-  static size_t granted[kMaxDevices] = {};
-  hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_tiled<true>), lds, granted);
-  if (e != hipSuccess) return e;
-  k_tiled<true><<<num_cus() / 8 * 8, kWaves * 64, lds, st>>>(xq, xs, offsets, P_local, pw1, pw1s, aq, as, nullptr, H, F,
-                                                          SingleRows{nullptr, nullptr, nullptr, 0u});
-  return hipGetLastError();
+                              bool nt_weights, hipStream_t st) {
+  const SingleRows none{nullptr, nullptr, nullptr, 0u};
+  return nt_weights ? run_tiled<true, kWeightNtLoads>(xq, xs, offsets, pw1, pw1s, aq, as, nullptr, H, F, P_local, none, st)
+                    : run_tiled<true, 0>(xq, xs, offsets, pw1, pw1s, aq, as, nullptr, H, F, P_local, none, st);
 }
 
 hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                               const uint8_t* pw2s, float* y, int H, int F, int P_local, SingleRows sr,
-                              hipStream_t st) {
-  const size_t lds = tiled_lds(P_local);
-  static size_t granted[kMaxDevices] = {};
-  hipError_t e = grant_lds(reinterpret_cast<const void*>(&k_tiled<false>), lds, granted);
-  if (e != hipSuccess) return e;
-  k_tiled<false><<<num_cus() / 8 * 8, kWaves * 64, lds, st>>>(aq, as, offsets, P_local, pw2, pw2s, nullptr, nullptr, y,
-                                                           H, F, sr);
-  return hipGetLastError();
+                              bool nt_weights, hipStream_t st) {
+  return nt_weights ? run_tiled<false, kWeightNtLoads>(aq, as, offsets, pw2, pw2s, nullptr, nullptr, y, H, F, P_local, sr, st)
+                    : run_tiled<false, 0>(aq, as, offsets, pw2, pw2s, nullptr, nullptr, y, H, F, P_local, sr, st);
 }
 
 }  // namespace moe

@@ -116,12 +116,14 @@ constexpr size_t kTiledLdsMax = 160 * 1024;
 bool tiled_fits(int H, int F, int P_local);
 // Large-M: persistent tiled kernels (grid = one block per CU, items decoded
 // on the device from offsets).
+// nt_weights: stream the weights with non-temporal loads (slots of about one
+// 128-token block, where no other block of the slot re-reads them).
 hipError_t launch_gemm1_tiled(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, const uint8_t* pw1,
                               const uint8_t* pw1s, uint8_t* aq, uint8_t* as, int H, int F, int P_local,
-                              hipStream_t st);
+                              bool nt_weights, hipStream_t st);
 hipError_t launch_gemm2_tiled(const uint8_t* aq, const uint8_t* as, const int32_t* offsets, const uint8_t* pw2,
                               const uint8_t* pw2s, float* y, int H, int F, int P_local, SingleRows sr,
-                              hipStream_t st);
+                              bool nt_weights, hipStream_t st);
 
 // Router projection (kernels_router.hip): logits [T, E] f32 = x [T, H] bf16 times
 // w_gate [E, H] bf16 transposed.  Plan: blocks of 128 experts x 16 ni tokens
