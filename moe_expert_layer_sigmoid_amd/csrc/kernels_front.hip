@@ -206,8 +206,9 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 // a2 + a3 (part 1): per chunk of 64 tokens, optionally remap logical -> physical
 // expert, then count.  One wavefront walks the chunk's pairs in (t, j) order,
 // 64 at a time: a pair's rank is the count of its slot before the group (an
-// LDS histogram) plus the lanes below it with the same slot (compared through
-// readlane), after which the group's pairs add themselves to the histogram.
+// LDS histogram) plus the lanes below it with the same slot (a ballot per
+// distinct local slot of the group), after which the group's pairs add
+// themselves to the histogram.
 // The histogram then gives the chunk's counts per slot.  Both results are
 // deterministic: the order of the adds only matters for their sum.
 // (Counting every slot against every pair, per thread, took 7 us of LDS
@@ -251,9 +252,21 @@ __global__ __launch_bounds__(256) void k_count(int T, int k, const int32_t* __re
       const int q = i < np ? s_phys[i] : -1;
       const bool inb = q >= 0 && q < P_total;  // slots outside the table count nowhere
       int r = inb ? s_hist[q] : 0;
-#pragma unroll 16
-      for (int j = 0; j < 64; ++j) r += (__builtin_amdgcn_readlane(q, j) == q) & (j < lane);
-      if (rank && i < np && q >= p0 && q < p0 + P_local) rank[pr0 + i] = r;
+      if (rank) {
+        // the lower lanes with the same slot, for the local pairs only: one
+        // round per distinct local slot of the group (its lanes found by
+        // ballot), not one per lane
+        const bool loc = i < np && q >= p0 && q < p0 + P_local;
+        uint64_t pending = __ballot(loc);
+        while (pending) {  // wave-uniform
+          const int lead = __builtin_ctzll(pending);
+          const int qv = __builtin_amdgcn_readlane(q, lead);
+          const uint64_t m = __ballot(q == qv);
+          if (q == qv) r += __popcll(m & ((1ull << lane) - 1ull));
+          pending &= ~m;
+        }
+        if (loc) rank[pr0 + i] = r;
+      }
       // every lane has read its count before any adds (one wavefront: LDS
       // operations run in order)
       if (inb) atomicAdd(&s_hist[q], 1);
