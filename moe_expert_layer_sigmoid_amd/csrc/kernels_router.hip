@@ -190,13 +190,23 @@ __global__ void __launch_bounds__(64 * kRouterWaves)
 }
 
 // logits = sum over s of part[s] (s ascending), n = T * E values; 16-byte
-// accesses when every split starts 16-byte aligned (n % 4 == 0).
+// accesses when every split starts 16-byte aligned (n % 4 == 0).  S is at
+// most SMAX (an instantiated bound: the loads of all splits are in flight at
+// once, so the bound is kept near S).
+template <int SMAX>
 __global__ void __launch_bounds__(256) k_router_reduce(const float* __restrict__ part, float* __restrict__ logits,
                                                        size_t n, int S) {
   const size_t n4 = (n & 3) == 0 ? n / 4 : 0;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
-    v4f s = reinterpret_cast<const v4f*>(part)[i];
-    for (int z = 1; z < S; ++z) s += reinterpret_cast<const v4f*>(part + (size_t)z * n)[i];
+    // every split's value in flight at once, then added in split order
+    v4f v[SMAX];
+#pragma unroll
+    for (int z = 0; z < SMAX; ++z)
+      v[z] = z < S ? reinterpret_cast<const v4f*>(part + (size_t)z * n)[i] : v4f{0.f, 0.f, 0.f, 0.f};
+    v4f s = v[0];
+#pragma unroll
+    for (int z = 1; z < SMAX; ++z)
+      if (z < S) s += v[z];
     reinterpret_cast<v4f*>(logits)[i] = s;
   }
   for (size_t i = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -260,7 +270,13 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, f
   const size_t n = (size_t)T * E;
   const size_t want = (n / 4 + 255) / 256 + 1;
   const int blocks = (int)(want < 2048 ? want : 2048);
-  hipLaunchKernelGGL(k_router_reduce, dim3(blocks), dim3(256), 0, st, partial, logits, n, p.splits);
+  static_assert(kRouterMaxSplits <= 16, "reduce instantiations");
+  if (p.splits <= 4)
+    hipLaunchKernelGGL(k_router_reduce<4>, dim3(blocks), dim3(256), 0, st, partial, logits, n, p.splits);
+  else if (p.splits <= 8)
+    hipLaunchKernelGGL(k_router_reduce<8>, dim3(blocks), dim3(256), 0, st, partial, logits, n, p.splits);
+  else
+    hipLaunchKernelGGL(k_router_reduce<16>, dim3(blocks), dim3(256), 0, st, partial, logits, n, p.splits);
   return hipGetLastError();
 }
 
